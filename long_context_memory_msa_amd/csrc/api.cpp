@@ -1,0 +1,419 @@
+// extern "C" entry points of libmsa: argument validation on the host, then
+// kernel launches on the caller's stream.  Declared and documented in
+// include/msa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/msa.h"
+#include "msa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MSA_OK;
+}
+
+int dev_fail(hipError_t e, const char *what) {
+  return fail(MSA_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define CHECK_PTR(p, al, name)                                                        \
+  do {                                                                                \
+    if (!(p)) return fail(MSA_ERR_ARG, "%s is null", name);                           \
+    if (!aligned((p), (al))) return fail(MSA_ERR_ARG, "%s is not %d-byte aligned", name, (int)(al)); \
+  } while (0)
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_bank(const msa_bank *b) {
+  if (!b) return fail(MSA_ERR_ARG, "bank is null");
+  if (b->dtype != MSA_F32 && b->dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "bank dtype %d", b->dtype);
+  if (b->n_docs < 1) return fail(MSA_ERR_ARG, "n_docs = %d", b->n_docs);
+  if (b->chunk < 1) return fail(MSA_ERR_ARG, "chunk = %d", b->chunk);
+  if (b->h_kv < 1) return fail(MSA_ERR_ARG, "h_kv = %d", b->h_kv);
+  if (b->d != 64 && b->d != 128) return fail(MSA_ERR_UNSUPPORTED, "head dim d = %d (64 or 128)", b->d);
+  if (b->d_r != 64 && b->d_r != 128) return fail(MSA_ERR_UNSUPPORTED, "router dim d_r = %d (64 or 128)", b->d_r);
+  if (b->h_r != 1 && b->h_r != 2 && b->h_r != 4 && b->h_r != 8 && b->h_r != 16)
+    return fail(MSA_ERR_UNSUPPORTED, "router heads h_r = %d (1, 2, 4, 8 or 16)", b->h_r);
+  if (b->h_r * b->d_r > 1024) return fail(MSA_ERR_UNSUPPORTED, "h_r * d_r = %d > 1024", b->h_r * b->d_r);
+  if (b->n_chunks < b->n_docs || b->n_chunks >= (int64_t)1 << 31)
+    return fail(MSA_ERR_ARG, "n_chunks = %lld (must be >= n_docs and < 2^31)", (long long)b->n_chunks);
+  if (b->max_doc_len < 1) return fail(MSA_ERR_ARG, "max_doc_len = %d", b->max_doc_len);
+  if (b->max_doc_chunks != (b->max_doc_len + b->chunk - 1) / b->chunk)
+    return fail(MSA_ERR_ARG, "max_doc_chunks = %d != ceil(max_doc_len / chunk)", b->max_doc_chunks);
+  if (b->n_chunks > (int64_t)b->n_docs * b->max_doc_chunks)
+    return fail(MSA_ERR_ARG, "n_chunks exceeds n_docs * max_doc_chunks");
+  CHECK_PTR(b->doc_tok_off, 8, "bank.doc_tok_off");
+  CHECK_PTR(b->doc_chunk_off, 8, "bank.doc_chunk_off");
+  CHECK_PTR(b->chunk_doc, 4, "bank.chunk_doc");
+  CHECK_PTR(b->kbar, 16, "bank.kbar");
+  CHECK_PTR(b->vbar, 16, "bank.vbar");
+  CHECK_PTR(b->krbar, 16, "bank.krbar");
+  CHECK_PTR(b->kr_inv_norm, 4, "bank.kr_inv_norm");
+  return MSA_OK;
+}
+
+int check_rope(const msa_rope *r, int d, int64_t need_pos) {
+  if (!r) return fail(MSA_ERR_ARG, "rope is null");
+  CHECK_PTR(r->cos, 4, "rope.cos");
+  CHECK_PTR(r->sin, 4, "rope.sin");
+  if (r->d != d) return fail(MSA_ERR_ARG, "rope.d = %d but head dim is %d", r->d, d);
+  if ((int64_t)r->max_pos < need_pos)
+    return fail(MSA_ERR_ARG, "rope.max_pos = %d < %lld positions needed", r->max_pos, (long long)need_pos);
+  return MSA_OK;
+}
+
+int check_attend_args(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, int32_t n_q, int32_t T,
+                      int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0, float scale, const msa_rope *rope,
+                      const void *O) {
+  CHECK_PTR(Q, 16, "Q");
+  CHECK_PTR(K_loc, 16, "K_loc");
+  CHECK_PTR(V_loc, 16, "V_loc");
+  CHECK_PTR(O, 16, "O");
+  if (n_q < 1) return fail(MSA_ERR_ARG, "n_q = %d", n_q);
+  if (T < 1 || L_loc < T) return fail(MSA_ERR_ARG, "need 1 <= T <= L_loc (T = %d, L_loc = %d)", T, L_loc);
+  if (h_q < b->h_kv || h_q % b->h_kv) return fail(MSA_ERR_ARG, "h_q = %d is not a multiple of h_kv = %d", h_q, b->h_kv);
+  if (k < 1 || k > b->n_docs || k > 256) return fail(MSA_ERR_ARG, "k = %d (need 1 <= k <= min(n_docs, 256))", k);
+  if (pos0 < 0) return fail(MSA_ERR_ARG, "pos0 = %d", pos0);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(MSA_ERR_ARG, "scale must be finite and > 0");
+  if ((int64_t)n_q * T * h_q / h_q != (int64_t)n_q * T) return fail(MSA_ERR_ARG, "sizes overflow");
+  if ((int64_t)n_q * b->h_kv * (((int64_t)T * (h_q / b->h_kv) + 15) / 16) * 64 >= ((int64_t)1 << 31))
+    return fail(MSA_ERR_ARG, "too many query rows");
+  return check_rope(rope, b->d, (int64_t)pos0 + L_loc);
+}
+
+msa::AttendArgs attend_args(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, int32_t n_q,
+                            int32_t T, int32_t L_loc, int32_t h_q, const int32_t *idx, int32_t k, int32_t pos0,
+                            float scale, const msa_rope *rope, void *O) {
+  msa::AttendArgs a;
+  a.dtype = b->dtype;
+  a.h_kv = b->h_kv;
+  a.d = b->d;
+  a.h_q = h_q;
+  a.n_chunks = b->n_chunks;
+  a.n_docs = b->n_docs;
+  a.doc_chunk_off = b->doc_chunk_off;
+  a.kbar = b->kbar;
+  a.vbar = b->vbar;
+  a.Q = Q;
+  a.K_loc = K_loc;
+  a.V_loc = V_loc;
+  a.n_q = n_q;
+  a.T = T;
+  a.L_loc = L_loc;
+  a.k = k;
+  a.pos0 = pos0;
+  a.scale = scale;
+  a.idx = idx;
+  a.cos = rope ? rope->cos : nullptr;
+  a.sin = rope ? rope->sin : nullptr;
+  a.O = O;
+  a.max_doc_chunks = b->max_doc_chunks;
+  return a;
+}
+
+msa::RouteArgs route_args(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, uint32_t *doc_keys,
+                          uint32_t *chunk_keys) {
+  msa::RouteArgs a;
+  a.dtype = b->dtype;
+  a.h_r = b->h_r;
+  a.d_r = b->d_r;
+  a.n_chunks = b->n_chunks;
+  a.n_docs = b->n_docs;
+  a.krbar = b->krbar;
+  a.kr_inv_norm = b->kr_inv_norm;
+  a.chunk_doc = b->chunk_doc;
+  a.qr = qr;
+  a.n_q = n_q;
+  a.t_r = t_r;
+  a.doc_keys = doc_keys;
+  a.chunk_keys = chunk_keys;
+  return a;
+}
+
+int check_route_args(const void *qr, int32_t n_q, int32_t t_r) {
+  CHECK_PTR(qr, 16, "QR");
+  if (n_q < 1 || t_r < 1) return fail(MSA_ERR_ARG, "need n_q >= 1 and t_r >= 1 (n_q = %d, t_r = %d)", n_q, t_r);
+  if ((int64_t)n_q * t_r > (int64_t)65535 * 16) return fail(MSA_ERR_ARG, "n_q * t_r = %lld > 1048560", (long long)n_q * t_r);
+  return MSA_OK;
+}
+
+size_t layer_ws(const msa_bank *b, int32_t n_q, int32_t T, int32_t L_loc, int32_t h_q, int32_t k) {
+  const size_t keys = align_up((size_t)n_q * b->n_docs * sizeof(uint32_t));
+  const size_t tk = align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
+  msa::AttendArgs a = attend_args(b, nullptr, nullptr, nullptr, n_q, T, L_loc, h_q, nullptr, k, 0, 1.f, nullptr, nullptr);
+  return keys + tk + align_up(msa::attend_ws_bytes(a));
+}
+
+}  // namespace
+
+namespace msa {
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+}  // namespace msa
+
+extern "C" {
+
+int msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char *msa_last_error(void) { return g_err.c_str(); }
+
+int msa_bank_layout(const int64_t *doc_lens, int32_t n_docs, int32_t chunk, int64_t *doc_tok_off,
+                    int64_t *doc_chunk_off, int64_t *n_chunks, int32_t *max_doc_len, int32_t *max_doc_chunks) {
+  if (!doc_lens || !doc_tok_off || !doc_chunk_off || !n_chunks || !max_doc_len || !max_doc_chunks)
+    return fail(MSA_ERR_ARG, "null pointer");
+  if (n_docs < 1) return fail(MSA_ERR_ARG, "n_docs = %d", n_docs);
+  if (chunk < 1) return fail(MSA_ERR_ARG, "chunk = %d", chunk);
+  int64_t tok = 0, ch = 0, mx = 0;
+  doc_tok_off[0] = 0;
+  doc_chunk_off[0] = 0;
+  for (int32_t i = 0; i < n_docs; ++i) {
+    const int64_t L = doc_lens[i];
+    if (L < 1 || L > (int64_t)1 << 30) return fail(MSA_ERR_ARG, "document %d has length %lld", i, (long long)L);
+    tok += L;
+    ch += (L + chunk - 1) / chunk;
+    mx = L > mx ? L : mx;
+    doc_tok_off[i + 1] = tok;
+    doc_chunk_off[i + 1] = ch;
+  }
+  if (ch >= (int64_t)1 << 31) return fail(MSA_ERR_ARG, "n_chunks = %lld >= 2^31", (long long)ch);
+  *n_chunks = ch;
+  *max_doc_len = (int32_t)mx;
+  *max_doc_chunks = (int32_t)((mx + chunk - 1) / chunk);
+  return ok();
+}
+
+int msa_rope_table(float *cos, float *sin, int32_t max_pos, int32_t d, double base, void *stream) {
+  try {
+    CHECK_PTR(cos, 4, "cos");
+    CHECK_PTR(sin, 4, "sin");
+    if (max_pos < 1) return fail(MSA_ERR_ARG, "max_pos = %d", max_pos);
+    if (d != 64 && d != 128) return fail(MSA_ERR_UNSUPPORTED, "d = %d (64 or 128)", d);
+    if (!(base > 0.0) || !std::isfinite(base)) return fail(MSA_ERR_ARG, "base must be finite and > 0");
+    hipError_t e = msa::launch_rope_table(cos, sin, max_pos, d, base, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : dev_fail(e, "rope_table");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void *KR, int32_t doc_begin,
+                    int32_t doc_end, const msa_rope *rope, void *stream) {
+  try {
+    int rc = check_bank(b);
+    if (rc) return rc;
+    CHECK_PTR(K, 16, "K");
+    CHECK_PTR(V, 16, "V");
+    CHECK_PTR(KR, 16, "KR");
+    if (!b->doc_tok_off_host || !b->doc_chunk_off_host) return fail(MSA_ERR_ARG, "pool needs the host offset arrays");
+    if (doc_begin < 0 || doc_end < doc_begin || doc_end > b->n_docs)
+      return fail(MSA_ERR_ARG, "document range [%d, %d) outside [0, %d)", doc_begin, doc_end, b->n_docs);
+    const int64_t *to = b->doc_tok_off_host, *co = b->doc_chunk_off_host;
+    if (to[0] != 0 || co[0] != 0 || co[b->n_docs] != b->n_chunks)
+      return fail(MSA_ERR_ARG, "host offsets do not describe a bank of n_chunks chunks");
+    int64_t mx = 0;
+    for (int32_t i = doc_begin; i < doc_end; ++i) {
+      const int64_t L = to[i + 1] - to[i];
+      if (L < 1) return fail(MSA_ERR_ARG, "document %d has length %lld", i, (long long)L);
+      if (co[i + 1] - co[i] != (L + b->chunk - 1) / b->chunk)
+        return fail(MSA_ERR_ARG, "document %d: chunk offsets inconsistent with its length", i);
+      mx = L > mx ? L : mx;
+    }
+    if (mx > b->max_doc_len) return fail(MSA_ERR_ARG, "a document is longer than max_doc_len");
+    rc = check_rope(rope, b->d, mx);
+    if (rc) return rc;
+    if (doc_end == doc_begin) return ok();
+    msa::PoolArgs a;
+    a.dtype = b->dtype;
+    a.h_kv = b->h_kv;
+    a.d = b->d;
+    a.h_r = b->h_r;
+    a.d_r = b->d_r;
+    a.chunk = b->chunk;
+    a.n_chunks = b->n_chunks;
+    a.doc_begin = doc_begin;
+    a.doc_end = doc_end;
+    a.slab_tok0 = to[doc_begin];
+    a.chunk_begin = co[doc_begin];
+    a.chunk_end = co[doc_end];
+    a.doc_tok_off = b->doc_tok_off;
+    a.doc_chunk_off = b->doc_chunk_off;
+    a.chunk_doc = b->chunk_doc;
+    a.K = K;
+    a.V = V;
+    a.KR = KR;
+    a.kbar = b->kbar;
+    a.vbar = b->vbar;
+    a.krbar = b->krbar;
+    a.kr_inv_norm = b->kr_inv_norm;
+    a.cos = rope->cos;
+    a.sin = rope->sin;
+    hipError_t e = msa::launch_pool(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : dev_fail(e, "pool");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *s_doc, float *s_chunk,
+                    void *stream) {
+  try {
+    int rc = check_bank(b);
+    if (rc) return rc;
+    rc = check_route_args(qr, n_q, t_r);
+    if (rc) return rc;
+    CHECK_PTR(s_doc, 4, "s_doc");
+    if (s_chunk && !aligned(s_chunk, 4)) return fail(MSA_ERR_ARG, "s_chunk is not 4-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const size_t nd = (size_t)n_q * b->n_docs, nc = (size_t)n_q * b->n_chunks;
+    uint32_t *dk = reinterpret_cast<uint32_t *>(s_doc);
+    uint32_t *ck = reinterpret_cast<uint32_t *>(s_chunk);
+    hipError_t e = msa::launch_fill_u32(dk, nd, 0u, s);
+    if (e == hipSuccess && ck) e = msa::launch_fill_u32(ck, nc, 0u, s);
+    if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, qr, n_q, t_r, dk, ck), s);
+    if (e == hipSuccess) e = msa::launch_keys_to_scores(dk, nd, s);
+    if (e == hipSuccess && ck) e = msa::launch_keys_to_scores(ck, nc, s);
+    return e == hipSuccess ? ok() : dev_fail(e, "route_score");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+size_t msa_topk_workspace_bytes(int32_t n_q, int32_t n_docs, int32_t k) {
+  if (n_q < 1 || n_docs < 1 || k < 1 || k > 256 || k > n_docs) return 0;
+  return msa::topk_ws_bytes(n_q, n_docs, k);
+}
+
+int msa_topk(const float *s_doc, int32_t n_q, int32_t n_docs, int32_t k, int32_t *idx, float *val, void *ws,
+             size_t ws_bytes, void *stream) {
+  try {
+    CHECK_PTR(s_doc, 4, "s_doc");
+    CHECK_PTR(idx, 4, "idx");
+    CHECK_PTR(val, 4, "val");
+    if (n_q < 1 || n_q > 65535) return fail(MSA_ERR_ARG, "n_q = %d (1..65535)", n_q);
+    if (n_docs < 1) return fail(MSA_ERR_ARG, "n_docs = %d", n_docs);
+    if (k < 1 || k > n_docs || k > 256) return fail(MSA_ERR_ARG, "k = %d (need 1 <= k <= min(n_docs, 256))", k);
+    const size_t need = msa::topk_ws_bytes(n_q, n_docs, k);
+    if (!ws || ws_bytes < need || !aligned(ws, 16))
+      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
+    hipError_t e = msa::launch_topk(s_doc, nullptr, n_q, n_docs, k, idx, val, ws, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : dev_fail(e, "topk");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+size_t msa_attend_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int32_t L_loc, int32_t h_q, int32_t k) {
+  if (!b || n_q < 1 || T < 1 || L_loc < T || b->h_kv < 1 || h_q < b->h_kv || h_q % b->h_kv || k < 1 ||
+      (b->d != 64 && b->d != 128))
+    return 0;
+  msa::AttendArgs a = attend_args(b, nullptr, nullptr, nullptr, n_q, T, L_loc, h_q, nullptr, k, 0, 1.f, nullptr, nullptr);
+  return msa::attend_ws_bytes(a);
+}
+
+int msa_sparse_attend(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, int32_t n_q, int32_t T,
+                      int32_t L_loc, int32_t h_q, const int32_t *idx, int32_t k, int32_t pos0, float scale,
+                      const msa_rope *rope, void *O, void *ws, size_t ws_bytes, void *stream) {
+  try {
+    int rc = check_bank(b);
+    if (rc) return rc;
+    rc = check_attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O);
+    if (rc) return rc;
+    CHECK_PTR(idx, 4, "idx");
+    msa::AttendArgs a = attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, idx, k, pos0, scale, rope, O);
+    const size_t need = msa::attend_ws_bytes(a);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 16)))
+      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
+    hipError_t e = msa::launch_attend(a, ws, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : dev_fail(e, "sparse_attend");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+size_t msa_layer_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q,
+                                 int32_t k) {
+  if (!b || n_q < 1 || T < 1 || t_r < 1 || L_loc < T || b->n_docs < 1 || b->h_kv < 1 || h_q < b->h_kv ||
+      h_q % b->h_kv || k < 1 || k > b->n_docs || k > 256 || (b->d != 64 && b->d != 128))
+    return 0;
+  return layer_ws(b, n_q, T, L_loc, h_q, k);
+}
+
+int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,
+                      int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0,
+                      float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
+                      size_t ws_bytes, void *const *stage_events, void *stream) {
+  try {
+    int rc = check_bank(b);
+    if (rc) return rc;
+    rc = check_route_args(QR, n_q, t_r);
+    if (rc) return rc;
+    rc = check_attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O);
+    if (rc) return rc;
+    if (n_q > 65535) return fail(MSA_ERR_ARG, "n_q = %d > 65535", n_q);
+    CHECK_PTR(idx, 4, "idx");
+    CHECK_PTR(val, 4, "val");
+    if (s_doc && !aligned(s_doc, 4)) return fail(MSA_ERR_ARG, "s_doc is not 4-byte aligned");
+    if (stage_events)
+      for (int i = 0; i < 4; ++i)
+        if (!stage_events[i]) return fail(MSA_ERR_ARG, "stage_events[%d] is null", i);
+    const size_t need = layer_ws(b, n_q, T, L_loc, h_q, k);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", need, ws_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    char *w = static_cast<char *>(ws);
+    uint32_t *keys = reinterpret_cast<uint32_t *>(w);
+    const size_t nd = (size_t)n_q * b->n_docs;
+    void *tk_ws = w + align_up(nd * sizeof(uint32_t));
+    void *at_ws = static_cast<char *>(tk_ws) + align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
+    auto rec = [&](int i) -> hipError_t {
+      return stage_events ? hipEventRecord((hipEvent_t)stage_events[i], s) : hipSuccess;
+    };
+    hipError_t e = msa::launch_fill_u32(keys, nd, 0u, s);
+    if (e == hipSuccess) e = rec(0);
+    if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, QR, n_q, t_r, keys, nullptr), s);
+    if (e == hipSuccess) e = rec(1);
+    if (e == hipSuccess) e = msa::launch_topk(nullptr, keys, n_q, b->n_docs, k, idx, val, tk_ws, s);
+    if (e == hipSuccess) e = rec(2);
+    if (e == hipSuccess)
+      e = msa::launch_attend(attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, idx, k, pos0, scale, rope, O), at_ws, s);
+    if (e == hipSuccess) e = rec(3);
+    if (e == hipSuccess && s_doc) {
+      e = hipMemcpyAsync(s_doc, keys, nd * sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess) e = msa::launch_keys_to_scores(reinterpret_cast<uint32_t *>(s_doc), nd, s);
+    }
+    return e == hipSuccess ? ok() : dev_fail(e, "layer_forward");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+}  // extern "C"

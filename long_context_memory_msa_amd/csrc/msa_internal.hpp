@@ -1,0 +1,76 @@
+// Internal launchers of the MSA library (host side, not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+int device_cu_count();  // compute units of the current device (cached per device)
+
+// ---- RoPE table ------------------------------------------------------------
+hipError_t launch_rope_table(float *cos, float *sin, int max_pos, int d, double base, hipStream_t s);
+
+// ---- pooling ---------------------------------------------------------------
+struct PoolArgs {
+  int dtype;                     // 0 fp32, 1 bf16
+  int h_kv, d, h_r, d_r, chunk;
+  int64_t n_chunks;              // bank chunks (row stride of kbar / vbar)
+  int doc_begin, doc_end;        // slab documents
+  int64_t slab_tok0;             // first token of doc_begin
+  int64_t chunk_begin, chunk_end;
+  const int64_t *doc_tok_off;    // device
+  const int64_t *doc_chunk_off;  // device
+  int32_t *chunk_doc;
+  const void *K, *V, *KR;        // slab tensors
+  void *kbar, *vbar, *krbar;
+  float *kr_inv_norm;
+  const float *cos, *sin;        // [max_pos][d/2]
+};
+hipError_t launch_pool(const PoolArgs &a, hipStream_t s);
+
+// ---- router scan -----------------------------------------------------------
+struct RouteArgs {
+  int dtype;
+  int h_r, d_r;
+  int64_t n_chunks;
+  int n_docs;
+  const void *krbar;
+  const float *kr_inv_norm;
+  const int32_t *chunk_doc;
+  const void *qr;                // [n_q][t_r][h_r][d_r]
+  int n_q, t_r;
+  uint32_t *doc_keys;            // [n_q][n_docs], zeroed before the scan
+  uint32_t *chunk_keys;          // [n_q][n_chunks] or null, zeroed before the scan
+};
+hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
+hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);
+hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s);  // in place
+
+// ---- top-k -----------------------------------------------------------------
+size_t topk_ws_bytes(int n_q, int n_docs, int k);
+// scores are either fp32 (keys == nullptr) or order-preserving keys (scores == nullptr)
+hipError_t launch_topk(const float *scores, const uint32_t *keys, int n_q, int n_docs, int k, int32_t *idx,
+                       float *val, void *ws, hipStream_t s);
+
+// ---- sparse attention ------------------------------------------------------
+struct AttendArgs {
+  int dtype;
+  int h_kv, d, h_q;
+  int64_t n_chunks;
+  int n_docs;
+  const int64_t *doc_chunk_off;
+  const void *kbar, *vbar;
+  const void *Q, *K_loc, *V_loc;
+  int n_q, T, L_loc, k, pos0;
+  float scale;
+  const int32_t *idx;
+  const float *cos, *sin;
+  void *O;
+  int max_doc_chunks;
+};
+int attend_splits(const AttendArgs &a);
+size_t attend_ws_bytes(const AttendArgs &a);
+hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s);
+
+}  // namespace msa

@@ -1,0 +1,228 @@
+// Top-k document selection (Lighthouse digest, Component 1: keep the Top-k
+// documents; hotdry blog, Top-k selection mechanism): the k largest scores
+// per query, sorted by descending score, ties to the lower document index.
+//
+// Every document becomes one distinct 64-bit composite
+//   (order-preserving score key << 32) | (0xFFFFFFFF - doc)
+// so "larger composite" is exactly "higher score, then lower index": the
+// selection is unique and independent of thread order.
+//   pass 1: one workgroup per (query, slice of 2048 documents) finds the
+//           slice's top-k composites by an 8-bit radix select (MSB first,
+//           stopping as soon as the boundary digit bin is taken whole);
+//   pass 2: one workgroup per query selects the top-k of the candidates
+//           the same way and sorts them (bitonic, in LDS).
+#include <algorithm>
+
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int TK_THREADS = 256;
+constexpr int TK_SLICE = 2048;
+constexpr int TK_MAX_K = 256;
+
+struct SelShared {
+  uint32_t hist[256];
+  int32_t wave_tot[TK_THREADS / 64];
+  uint32_t bin;      // chosen digit
+  uint32_t above;    // elements with a larger digit among the matching ones
+  uint32_t in_bin;   // elements in the chosen bin
+};
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, int64_t i) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// Exclusive prefix sum over the block; returns this thread's offset, *total.
+__device__ int block_excl_scan(int v, SelShared &sh, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh.wave_tot[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < TK_THREADS / 64; ++w) {
+    if (w < wave) base += sh.wave_tot[w];
+    tot += sh.wave_tot[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// Radix select of the `need` largest of n distinct composites get(i), i < n.
+// Returns (shift, prefix): the selected elements are those with
+// (v >> shift) >= (prefix >> shift); exactly `need` of them.
+template <typename Get>
+__device__ void radix_select(Get get, int64_t n, uint32_t need, SelShared &sh, int *out_shift, uint64_t *out_prefix) {
+  uint64_t prefix = 0;
+  int shift = 56;
+  for (;; shift -= 8) {
+    for (int b = threadIdx.x; b < 256; b += TK_THREADS) sh.hist[b] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += TK_THREADS) {
+      const uint64_t v = get(i);
+      const bool match = (shift == 56) || ((v ^ prefix) >> (shift + 8)) == 0;
+      if (match) atomicAdd(&sh.hist[(v >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l owns bins 255-4l .. 252-4l (descending digit order)
+      const int lane = threadIdx.x;
+      uint32_t c[4], s = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = sh.hist[255 - 4 * lane - j];
+        s += c[j];
+      }
+      uint32_t incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const unsigned long long m = __ballot(incl >= need);
+      const int first = __ffsll((long long)m) - 1;
+      if (lane == first) {
+        uint32_t cum = incl - s;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= need) {
+            sh.bin = 255 - 4 * lane - j;
+            sh.above = cum;
+            sh.in_bin = c[j];
+            break;
+          }
+          cum += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sh.bin, above = sh.above, in_bin = sh.in_bin;
+    __syncthreads();
+    prefix |= (uint64_t)bin << shift;
+    need -= above;
+    if (in_bin == need || shift == 0) break;
+  }
+  *out_shift = shift;
+  *out_prefix = prefix;
+}
+
+template <bool FROM_KEYS>
+__global__ __launch_bounds__(TK_THREADS) void topk_pass1(const float *scores, const uint32_t *keys, int n_docs, int k,
+                                                           int n_slices, uint64_t *cand) {
+  __shared__ SelShared sh;
+  const int q = blockIdx.y, slice = blockIdx.x;
+  const int64_t lo = (int64_t)slice * TK_SLICE;
+  const int64_t n = std::min<int64_t>(TK_SLICE, n_docs - lo);
+  const uint32_t kk = (uint32_t)std::min<int64_t>(k, n);
+  const int64_t rowbase = (int64_t)q * n_docs + lo;
+  auto get = [&](int64_t i) -> uint64_t {
+    const uint32_t key = FROM_KEYS ? keys[rowbase + i] : score_key(scores[rowbase + i]);
+    return composite(key, lo + i);
+  };
+  int shift;
+  uint64_t prefix;
+  radix_select(get, n, kk, sh, &shift, &prefix);
+  uint64_t *out = cand + ((int64_t)q * n_slices + slice) * k;
+  // compaction in index order (items per thread are strided by the block size)
+  for (int64_t base = 0; base < n; base += TK_THREADS) {
+    const int64_t i = base + threadIdx.x;
+    uint64_t v = 0;
+    int f = 0;
+    if (i < n) {
+      v = get(i);
+      f = (v >> shift) >= (prefix >> shift);
+    }
+    int tot;
+    const int pos = block_excl_scan(f, sh, &tot);
+    if (f) out[pos] = v;
+    out += tot;
+  }
+  for (int j = kk + threadIdx.x; j < k; j += TK_THREADS) cand[((int64_t)q * n_slices + slice) * k + j] = 0;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_pass2(const uint64_t *cand, int64_t n_cand, int k, int kpad,
+                                                           int32_t *idx, float *val) {
+  __shared__ SelShared sh;
+  __shared__ uint64_t sel[TK_MAX_K];
+  const int q = blockIdx.x;
+  const uint64_t *c = cand + (int64_t)q * n_cand;
+  auto get = [&](int64_t i) -> uint64_t { return c[i]; };
+  int shift;
+  uint64_t prefix;
+  radix_select(get, n_cand, (uint32_t)k, sh, &shift, &prefix);
+  for (int j = threadIdx.x; j < kpad; j += TK_THREADS) sel[j] = 0;
+  __syncthreads();
+  int written = 0;
+  for (int64_t base = 0; base < n_cand; base += TK_THREADS) {
+    const int64_t i = base + threadIdx.x;
+    uint64_t v = 0;
+    int f = 0;
+    if (i < n_cand) {
+      v = c[i];
+      f = v != 0 && (v >> shift) >= (prefix >> shift);
+    }
+    int tot;
+    const int pos = block_excl_scan(f, sh, &tot);
+    if (f) sel[written + pos] = v;
+    written += tot;
+  }
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= kpad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < kpad; i += TK_THREADS) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t x = sel[i], y = sel[j];
+          const bool desc = (i & size) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            sel[i] = y;
+            sel[j] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = threadIdx.x; r < k; r += TK_THREADS) {
+    const uint64_t v = sel[r];
+    idx[(int64_t)q * k + r] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
+    val[(int64_t)q * k + r] = key_score((uint32_t)(v >> 32));
+  }
+}
+
+int n_slices_for(int n_docs) { return (n_docs + TK_SLICE - 1) / TK_SLICE; }
+
+}  // namespace
+
+size_t topk_ws_bytes(int n_q, int n_docs, int k) {
+  return (size_t)n_q * n_slices_for(n_docs) * k * sizeof(uint64_t);
+}
+
+hipError_t launch_topk(const float *scores, const uint32_t *keys, int n_q, int n_docs, int k, int32_t *idx, float *val,
+                       void *ws, hipStream_t s) {
+  const int ns = n_slices_for(n_docs);
+  uint64_t *cand = static_cast<uint64_t *>(ws);
+  dim3 g1(ns, n_q);
+  if (keys)
+    hipLaunchKernelGGL(topk_pass1<true>, g1, dim3(TK_THREADS), 0, s, scores, keys, n_docs, k, ns, cand);
+  else
+    hipLaunchKernelGGL(topk_pass1<false>, g1, dim3(TK_THREADS), 0, s, scores, keys, n_docs, k, ns, cand);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int kpad = 1;
+  while (kpad < k) kpad <<= 1;
+  hipLaunchKernelGGL(topk_pass2, dim3(n_q), dim3(TK_THREADS), 0, s, cand, (int64_t)ns * k, k, kpad, idx, val);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,167 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/msa.h declares, and rejects invalid arguments on the host (with a
+message, before any HIP call) -- no GPU needed."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import long_context_memory_msa_amd as msa
+from long_context_memory_msa_amd import _lib as L
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def declared_symbols():
+    text = (ROOT / "include" / "msa.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(str(L.LIB_PATH))
+    for n in names:
+        assert hasattr(lib, n), n
+        assert hasattr(L, n), f"binding lacks {n}"
+
+
+def test_abi_version_and_empty_error():
+    assert msa.msa_abi_version() == 1
+    msa.msa_bank_layout([3], 2)
+    assert msa.msa_last_error() == ""
+
+
+def test_bank_layout_host_helper():
+    lens = np.array([5, 128, 129, 1, 300])
+    lay = msa.msa_bank_layout(lens, 128)
+    assert lay["doc_tok_off"].tolist() == [0, 5, 133, 262, 263, 563]
+    assert lay["doc_chunk_off"].tolist() == [0, 1, 2, 4, 5, 8]
+    assert lay["n_chunks"] == 8 and lay["max_doc_len"] == 300 and lay["max_doc_chunks"] == 3
+    for bad_lens, chunk in (([3, 0, 2], 4), ([], 4), ([4], 0)):
+        with pytest.raises(msa.MsaError) as e:
+            msa.msa_bank_layout(bad_lens, chunk)
+        assert e.value.code == L.MSA_ERR_ARG
+
+
+class _Fake:
+    """Stands in for a device tensor: only its address is ever read."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+A = _Fake(0x10000)      # 16-byte aligned, never dereferenced (validation fails first)
+MIS = _Fake(0x10004)    # misaligned
+
+
+def _bank(**over):
+    lay = msa.msa_bank_layout([512] * 4, 128)
+    b = L.MsaBank(L.MSA_BF16, 4, 128, 8, 128, 8, 128, 512, 4, 0, lay["n_chunks"], A.addr, A.addr, None, None,
+                  A.addr, A.addr, A.addr, A.addr, A.addr)
+    for k, v in over.items():
+        setattr(b, k, v)
+    return b
+
+
+def _rope(**over):
+    r = L.MsaRope(A.addr, A.addr, 4096, 128)
+    for k, v in over.items():
+        setattr(r, k, v)
+    return r
+
+
+def _code(fn, *a, **kw):
+    with pytest.raises(msa.MsaError) as e:
+        fn(*a, **kw)
+    assert msa.msa_last_error() != ""
+    return e.value.code
+
+
+def test_rope_table_validation():
+    assert _code(msa.msa_rope_table, None, A, 16, 128, 1e4, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_rope_table, A, A, 16, 96, 1e4, 0) == L.MSA_ERR_UNSUPPORTED
+    assert _code(msa.msa_rope_table, A, A, 0, 128, 1e4, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_rope_table, A, A, 16, 128, -1.0, 0) == L.MSA_ERR_ARG
+
+
+def test_bank_validation():
+    for over, code in (({"dtype": 7}, L.MSA_ERR_UNSUPPORTED), ({"d": 96}, L.MSA_ERR_UNSUPPORTED),
+                       ({"h_r": 3}, L.MSA_ERR_UNSUPPORTED), ({"n_docs": 0}, L.MSA_ERR_ARG),
+                       ({"max_doc_chunks": 9}, L.MSA_ERR_ARG), ({"kbar": None}, L.MSA_ERR_ARG),
+                       ({"krbar": MIS.addr}, L.MSA_ERR_ARG), ({"n_chunks": 1}, L.MSA_ERR_ARG)):
+        assert _code(msa.msa_route_score, _bank(**over), A, 1, 1, A, None, 0) == code, over
+
+
+def test_route_validation():
+    assert _code(msa.msa_route_score, _bank(), None, 1, 1, A, None, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), A, 0, 1, A, None, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), A, 1, 0, A, None, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), MIS, 1, 1, A, None, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), A, 1, 1, None, None, 0) == L.MSA_ERR_ARG
+
+
+def test_topk_validation_and_workspace():
+    assert msa.msa_topk_workspace_bytes(2, 5000, 16) == 2 * 3 * 16 * 8
+    assert msa.msa_topk_workspace_bytes(1, 10, 11) == 0
+    assert _code(msa.msa_topk, A, 1, 10, 11, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG      # k > n_docs
+    assert _code(msa.msa_topk, A, 1, 1000, 257, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG   # k > 256
+    assert _code(msa.msa_topk, A, 1, 1000, 0, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_topk, A, 1, 5000, 16, A, A, A, 100, 0) == L.MSA_ERR_WORKSPACE
+    assert _code(msa.msa_topk, A, 1, 5000, 16, A, A, None, 1 << 20, 0) == L.MSA_ERR_WORKSPACE
+
+
+def test_attend_validation():
+    b = _bank()
+    ok = dict(Q=A, K_loc=A, V_loc=A, n_q=1, T=4, L_loc=8, h_q=32, idx=A, k=2, pos0=2, scale=0.1, rope=_rope(),
+              O=A, ws=A, ws_bytes=1 << 30)
+
+    def call(**over):
+        a = {**ok, **over}
+        return _code(msa.msa_sparse_attend, b, a["Q"], a["K_loc"], a["V_loc"], a["n_q"], a["T"], a["L_loc"], a["h_q"],
+                     a["idx"], a["k"], a["pos0"], a["scale"], a["rope"], a["O"], a["ws"], a["ws_bytes"], 0)
+
+    assert call(T=9) == L.MSA_ERR_ARG                     # T > L_loc
+    assert call(h_q=12) == L.MSA_ERR_ARG                  # not a multiple of h_kv
+    assert call(k=5) == L.MSA_ERR_ARG                     # k > n_docs
+    assert call(Q=None) == L.MSA_ERR_ARG
+    assert call(O=MIS) == L.MSA_ERR_ARG
+    assert call(scale=float("nan")) == L.MSA_ERR_ARG
+    assert call(rope=_rope(max_pos=9)) == L.MSA_ERR_ARG   # pos0 + L_loc = 10 > 9
+    assert call(rope=_rope(d=64)) == L.MSA_ERR_ARG
+    assert call(idx=None) == L.MSA_ERR_ARG
+    assert msa.msa_attend_workspace_bytes(b, 1, 9, 8, 32, 2) == 0
+
+
+def test_pool_validation():
+    lay = msa.msa_bank_layout([512] * 4, 128)
+    tok, ch = lay["doc_tok_off"], lay["doc_chunk_off"]
+    b = _bank(doc_tok_off_host=tok.ctypes.data, doc_chunk_off_host=ch.ctypes.data)
+    r = _rope(max_pos=512)
+    assert _code(msa.msa_pool_memory, b, A, A, A, 0, 5, r, 0) == L.MSA_ERR_ARG          # range beyond n_docs
+    assert _code(msa.msa_pool_memory, b, A, A, A, 2, 1, r, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_pool_memory, b, None, A, A, 0, 1, r, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_pool_memory, _bank(), A, A, A, 0, 1, r, 0) == L.MSA_ERR_ARG    # no host offsets
+    assert _code(msa.msa_pool_memory, b, A, A, A, 0, 1, _rope(max_pos=100), 0) == L.MSA_ERR_ARG
+    bad = ch.copy()
+    bad[2] += 1
+    b2 = _bank(doc_tok_off_host=tok.ctypes.data, doc_chunk_off_host=bad.ctypes.data)
+    assert _code(msa.msa_pool_memory, b2, A, A, A, 0, 4, r, 0) == L.MSA_ERR_ARG
+
+
+def test_layer_validation():
+    b = _bank()
+    r = _rope()
+    args = [b, A, A, A, A, 1, 4, 4, 8, 32, 2, 2, 0.1, r, A, A, A, None, A, 1 << 30]
+    assert _code(msa.msa_layer_forward, *args[:19], 16, stream=0) == L.MSA_ERR_WORKSPACE
+    bad = list(args)
+    bad[7] = 0                                              # t_r = 0
+    assert _code(msa.msa_layer_forward, *bad, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_layer_forward, *args, stage_events=[A.addr, 0, A.addr, A.addr], stream=0) == L.MSA_ERR_ARG
+    assert msa.msa_layer_workspace_bytes(b, 1, 4, 4, 8, 32, 2) > 0

@@ -1,0 +1,264 @@
+"""GPU parity of every hot-path step against the fp64 oracle, at sizes the
+oracle finishes in seconds (several tiles, ragged tails, all five workload
+shapes), through the C ABI.
+
+Tolerances (written here, applied elementwise):
+  pooled fp32      per (chunk, head) row: max |gpu - exact| <= 1e-5 * max |exact row|
+  pooled bf16      |gpu - exact| <= one bf16 spacing at the exact value + 1e-5 * max |exact row|
+  inverse norms    |gpu - 1/||gpu row||| <= 2e-6 relative (property); vs oracle 1e-5 (fp32) / 2e-4 (bf16)
+  router scores    |gpu - oracle| <= 2e-3 (s_chunk and s_doc)
+  top-k            bit-exact on identical scores; on scores the GPU computed itself the set is
+                   identical where the oracle's k-th vs (k+1)-th gap exceeds 4e-3, else every pick
+                   is within 4e-3 of the oracle's k-th score
+  attention        max |gpu - oracle| <= 2e-2 and mean <= 1e-3
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import rng, workloads as W
+from long_context_memory_msa_amd import _lib as L, memory as M
+
+from gpu_common import (assert_attention_close, bf16_spacing, dev, gpu_bank_from_oracle, gpu_bank_pooled, host,
+                        host_inputs, log, oracle_bank, query_views, run_layer, topk_set_valid)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _wl(cfg, bank_tokens=None, **kw):
+    w = W.make_workload(cfg, bank_tokens=bank_tokens)
+    return dataclasses.replace(w, **kw) if kw else w
+
+
+# small versions of the five workloads: (config, bank tokens) -- ragged where the law allows
+SMALL = {
+    "cfg0": (0, None),
+    "cfg1": (1, None),
+    "cfg2": (2, 150_000),
+    "cfg3": (3, 700_000),
+    "cfg4": (4, 120_000),
+}
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,base,max_pos", [(128, 10000.0, 8192), (64, 10000.0, 600), (128, 500000.0, 4096)])
+def test_rope_table(device, d, base, max_pos):
+    log(f"rope d={d} base={base} max_pos={max_pos}")
+    r = M.Rope(max_pos, d, base, device)
+    torch.cuda.synchronize()
+    c, s = O.rope_cos_sin(np.arange(max_pos), d, base)
+    assert np.abs(host(r.cos) - c).max() <= 6e-8
+    assert np.abs(host(r.sin) - s).max() <= 6e-8
+
+
+def _check_pool(w, ob, bank):
+    kb, vb, krb = host(bank.kbar), host(bank.vbar), host(bank.krbar)
+    for got, name in ((kb, "kbar"), (vb, "vbar"), (krb, "krbar")):
+        exact = ob[name + "_exact"]
+        if w.dtype == "f32":
+            err = np.abs(got - exact).max(axis=-1)
+            ref = np.abs(exact).max(axis=-1)
+            assert np.all(err <= 1e-5 * ref + 1e-30), f"{name}: worst row rel err {np.max(err / ref):.3g}"
+        else:
+            # one bf16 spacing (the final rounding of a perturbed fp32 mean may land on the
+            # neighbour) plus the fp32 accumulation slack of the row, as in the fp32 bound
+            slack = 1e-5 * np.abs(exact).max(axis=-1, keepdims=True)
+            err = np.abs(got - exact)
+            bad = err > bf16_spacing(exact) + slack
+            assert not bad.any(), f"{name}: {bad.sum()} elements beyond one bf16 spacing (worst {err[bad].max():.3g})"
+    inv = host(bank.kr_inv_norm)
+    own = 1.0 / np.linalg.norm(krb, axis=-1)
+    assert np.all(np.abs(inv - own) <= 2e-6 * own)
+    tol = 1e-5 if w.dtype == "f32" else 2e-4
+    assert np.all(np.abs(inv - ob["kr_inv_norm"]) <= tol * ob["kr_inv_norm"])
+    assert np.array_equal(bank.chunk_doc.cpu().numpy(), ob["chunk_doc"])
+
+
+@pytest.mark.parametrize("name,n_slabs", [("cfg0", 1), ("cfg1", 2), ("cfg2", 3), ("cfg4", 1)])
+def test_pool(device, name, n_slabs):
+    cfg, bt = SMALL[name]
+    w = _wl(cfg, bt)
+    log(f"pool {name} docs={w.n_docs} chunks={w.n_chunks} slabs={n_slabs}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    bank, _ = gpu_bank_pooled(w, K, V, KR, device, n_slabs)
+    _check_pool(w, ob, bank)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pool_edge_lengths(device, dtype):
+    # lengths around the chunk size, single-token documents, one long document
+    base = _wl(0) if dtype == "f32" else _wl(1)
+    C = base.chunk
+    lens = np.array([1, C - 1, C, C + 1, 3 * C + 5, 2, C // 2, 7 * C], dtype=np.int64)
+    w = dataclasses.replace(base, doc_lens=lens, gold=np.zeros((1, 0), np.int64))
+    log(f"pool edge {dtype} lens={lens.tolist()}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    bank, _ = gpu_bank_pooled(w, K, V, KR, device, 2)
+    _check_pool(w, ob, bank)
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,t_r,n_q", [("cfg0", 16, 1), ("cfg1", 128, 1), ("cfg1", 1, 1), ("cfg1", 5, 3),
+                                          ("cfg1", 40, 2), ("cfg2", 256, 1), ("cfg3", 1, 16)])
+def test_route_isolated(device, name, t_r, n_q):
+    cfg, bt = SMALL[name]
+    w = _wl(cfg, bt)
+    if n_q != w.n_q:
+        w = dataclasses.replace(w, n_q=n_q, gold=np.zeros((n_q, 0), np.int64))
+    log(f"route {name} t_r={t_r} n_q={n_q} chunks={w.n_chunks}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    QRh = qi["QR"][:, :t_r]
+    S = O.chunk_scores(QRh, ob["krbar"])
+    sd = O.doc_scores(S, ob["doc_chunk_off"])
+    bank, _ = gpu_bank_from_oracle(w, ob, device)
+    s_doc = torch.empty((n_q, w.n_docs), dtype=torch.float32, device=device)
+    s_chunk = torch.empty((n_q, w.n_chunks), dtype=torch.float32, device=device)
+    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc, s_chunk)
+    torch.cuda.synchronize()
+    assert np.abs(host(s_chunk) - S).max() <= 2e-3
+    assert np.abs(host(s_doc) - sd).max() <= 2e-3
+    # without the optional chunk output
+    s_doc2 = torch.empty_like(s_doc)
+    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(s_doc, s_doc2)
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n_q,n_docs,k", [(1, 7, 1), (1, 7, 7), (3, 2048, 16), (2, 5000, 256), (16, 23048, 16),
+                                          (4, 4099, 64), (1, 300, 256)])
+def test_topk_isolated(device, n_q, n_docs, k):
+    log(f"topk n_q={n_q} n_docs={n_docs} k={k}")
+    s = W.scores_for_topk(1000 + n_docs + k, n_q, n_docs)
+    want = O.topk(s.astype(np.float64), k)
+    sd = torch.from_numpy(s).to(device)
+    idx = torch.empty((n_q, k), dtype=torch.int32, device=device)
+    val = torch.empty((n_q, k), dtype=torch.float32, device=device)
+    nb = L.msa_topk_workspace_bytes(n_q, n_docs, k)
+    ws = M.workspace(nb, device)
+    L.msa_topk(sd, n_q, n_docs, k, idx, val, ws, nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), want["idx"])
+    assert np.array_equal(val.cpu().numpy().astype(np.float64), want["val"])
+
+
+# ---------------------------------------------------------------------------
+def _attend_case(w, device, idx_h, T=None, L_loc=None):
+    T = T or w.T
+    L_loc = L_loc or w.L_loc
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    Qh = qi["Q"][:, L_loc - T:L_loc]
+    Klh, Vlh = qi["K_loc"][:, :L_loc], qi["V_loc"][:, :L_loc]
+    want = O.attend(Qh, Klh, Vlh, ob["kbar"], ob["vbar"], ob["doc_chunk_off"], idx_h, w.pos0, base=w.rope_base)
+    bank, rope = gpu_bank_from_oracle(w, ob, device)
+    k = idx_h.shape[1]
+    out = torch.empty((w.n_q, T, w.h_q, w.d), dtype=M.TORCH_DTYPE[w.dtype], device=device)
+    nb = L.msa_attend_workspace_bytes(bank.c, w.n_q, T, L_loc, w.h_q, k)
+    ws = M.workspace(nb, device)
+    L.msa_sparse_attend(bank.c, dev(Qh, w.dtype, device), dev(Klh, w.dtype, device), dev(Vlh, w.dtype, device),
+                        w.n_q, T, L_loc, w.h_q, torch.from_numpy(idx_h.astype(np.int32)).to(device), k, w.pos0,
+                        L.default_scale(w.d), rope.c, out, ws, nb)
+    torch.cuda.synchronize()
+    return host(out), want
+
+
+@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2", "cfg3"])
+def test_attend_isolated(device, name):
+    cfg, bt = SMALL[name]
+    w = _wl(cfg, bt)
+    g = np.random.default_rng(7)
+    idx_h = np.stack([g.choice(w.n_docs, size=w.k, replace=False) for _ in range(w.n_q)])
+    log(f"attend {name} n_q={w.n_q} T={w.T} L_loc={w.L_loc} k={w.k}")
+    got, want = _attend_case(w, device, idx_h)
+    e = assert_attention_close(got, want)
+    log(f"  max {e[0]:.3g} mean {e[1]:.3g}")
+
+
+def test_attend_all_documents_is_dense(device):
+    # k = n_docs: attention over the whole compressed memory plus the local context
+    w = _wl(0)
+    idx_h = np.random.default_rng(3).permutation(w.n_docs)[None, :]
+    w = dataclasses.replace(w, k=w.n_docs, pos0=w.n_docs)
+    got, want = _attend_case(w, device, idx_h)
+    assert_attention_close(got, want)
+
+
+@pytest.mark.parametrize("T,L_loc", [(1, 1), (1, 37), (3, 70), (50, 50), (64, 640)])
+def test_attend_shapes(device, T, L_loc):
+    # decode and partial prefill over long local contexts (causal tails, several key tiles)
+    w = _wl(1)
+    w = dataclasses.replace(w, T=T, L_loc=L_loc, T_route=min(L_loc, 128), rounds=1, append=0)
+    idx_h = np.random.default_rng(T + L_loc).choice(w.n_docs, size=(1, w.k), replace=False)
+    got, want = _attend_case(w, device, idx_h, T, L_loc)
+    assert_attention_close(got, want)
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2", "cfg3"])
+def test_layer_end_to_end(device, name):
+    cfg, bt = SMALL[name]
+    w = _wl(cfg, bt)
+    log(f"layer {name} docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q} T={w.T}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    want = O.layer_forward(qi["QR"][:, w.L_loc - w.T_route:w.L_loc], qi["Q"][:, w.L_loc - w.T:w.L_loc],
+                           qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], ob, w.k, w.pos0, base=w.rope_base)
+    bank, rope = gpu_bank_pooled(w, K, V, KR, device, 2)
+    QR, Q, Kl, Vl = query_views(w, qi, device)
+    out, idx, val, s_doc = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+    sd = host(s_doc)
+    assert np.abs(sd - want["s_doc"]).max() <= 2e-3
+    gi = idx.cpu().numpy()
+    # the values returned are the GPU's own document scores of the picks, in order
+    assert np.array_equal(val.cpu().numpy(), s_doc.cpu().numpy()[np.arange(w.n_q)[:, None], gi])
+    assert np.all(np.diff(val.cpu().numpy(), axis=1) <= 0)
+    same = True
+    for q in range(w.n_q):
+        if want["gap"][q] > 4e-3:
+            assert set(gi[q].tolist()) == set(want["idx"][q].tolist())
+        same &= set(gi[q].tolist()) == set(want["idx"][q].tolist())
+    topk_set_valid(gi, want["s_doc"], w.k)
+    for q in range(w.n_q):
+        if w.gold.size and set(w.gold[q].tolist()) <= set(want["idx"][q].tolist()):
+            assert set(w.gold[q].tolist()) <= set(gi[q].tolist()), "planted gold not recovered"
+    if same:
+        assert_attention_close(host(out), want["O"])
+
+
+def test_layer_equals_composition_and_is_deterministic(device):
+    w = _wl(3, 300_000)
+    qi, K, V, KR = host_inputs(w)
+    bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
+    QR, Q, Kl, Vl = query_views(w, qi, device)
+    o1, i1, v1, s1 = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+    o2, i2, v2, s2 = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+    assert torch.equal(o1, o2) and torch.equal(i1, i2) and torch.equal(v1, v2) and torch.equal(s1, s2)
+    # the same three steps through the individual entry points
+    s_doc = torch.empty_like(s1)
+    L.msa_route_score(bank.c, QR, w.n_q, w.T_route, s_doc, None)
+    idx = torch.empty_like(i1)
+    val = torch.empty_like(v1)
+    nb = L.msa_topk_workspace_bytes(w.n_q, w.n_docs, w.k)
+    ws = M.workspace(nb, device)
+    L.msa_topk(s_doc, w.n_q, w.n_docs, w.k, idx, val, ws, nb)
+    out = torch.empty_like(o1)
+    nb2 = L.msa_attend_workspace_bytes(bank.c, w.n_q, w.T, w.L_loc, w.h_q, w.k)
+    ws2 = M.workspace(nb2, device)
+    L.msa_sparse_attend(bank.c, Q, Kl, Vl, w.n_q, w.T, w.L_loc, w.h_q, idx, w.k, w.pos0, L.default_scale(w.d),
+                        rope.c, out, ws2, nb2)
+    torch.cuda.synchronize()
+    assert torch.equal(s_doc, s1) and torch.equal(idx, i1) and torch.equal(val, v1) and torch.equal(out, o1)
