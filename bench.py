@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of one MSA routed layer over a 100M-token memory bank on one MI355X.
+
+Workload (decode): 100,000,000 bank tokens in documents of U[512, 8192]
+tokens, chunk 128 (about 793K chunks), 8 router heads x 128, 32 query / 8 KV
+heads x 128, bf16 storage with fp32 accumulation, 16 independent queries x 1
+decode token, k = 16, 8 planted gold documents per query.  The pooled bank
+(Kbar^R 1.6 GB, Kbar/Vbar 3.2 GB) is resident in HBM before timing; the raw
+per-token tensors (614 GB) are generated on the device and pooled slab by slab
+beforehand (the offline stage).
+
+A step is one msa_layer_forward: router scan with the fused document max,
+top-k, sparse attention (plus split merge).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import resource
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "memory tokens routed/sec/GPU + MSA layer latency @100M-token bank; % HBM peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+class Events:
+    """Raw hipEvent_t handles (timing enabled) for msa_layer_forward's stage_events."""
+
+    def __init__(self, n: int):
+        self.hip = _hip()
+        self.h = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.h.append(e.value)
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for e in self.h:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(w, qi, n_docs: int) -> dict:
+    """The fp64 oracle's layer forward on the first ``n_docs`` documents of the
+    bank (pooled-shape synthetic values; the oracle's time does not depend on
+    them), on this host's cores."""
+    import numpy as np
+
+    import oracle as O
+    from synth import rng
+
+    n_docs = w.n_docs if n_docs < 0 else min(n_docs, w.n_docs)
+    lens = w.doc_lens[:n_docs]
+    lay = O.bank_layout(lens, w.chunk)
+    N = lay["n_chunks"]
+    g = 1.0 / np.sqrt(w.chunk)
+    bank = {
+        "krbar": rng.normal_stored(rng.stream_key(w.seed, rng.ROLE_POOLED_KR), 0, N * w.h_r * w.d_r,
+                                   w.dtype).reshape(N, w.h_r, w.d_r) * np.float32(g),
+        "kbar": rng.normal_stored(rng.stream_key(w.seed, rng.ROLE_POOLED_K), 0, N * w.h_kv * w.d,
+                                  w.dtype).reshape(w.h_kv, N, w.d) * np.float32(g),
+        "vbar": rng.normal_stored(rng.stream_key(w.seed, rng.ROLE_POOLED_V), 0, N * w.h_kv * w.d,
+                                  w.dtype).reshape(w.h_kv, N, w.d) * np.float32(g),
+        "doc_chunk_off": lay["doc_chunk_off"],
+    }
+    QR = qi["QR"][:, w.L_loc - w.T_route:w.L_loc]
+    Q = qi["Q"][:, w.L_loc - w.T:w.L_loc]
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    O.layer_forward(QR, Q, qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], bank, w.k, w.pos0, base=w.rope_base)
+    dt = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    tokens = int(lens.sum())
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": max(1, round(cpu / dt)),
+        "kind": "oracle",
+        "sample": (f"oracle layer_forward (route + document max + top-k + attention, fp64 NumPy) over the first "
+                   f"{n_docs} documents ({tokens} tokens, {N} chunks) of the same bank layout and query batch; "
+                   f"{dt:.1f} s wall, {cpu:.1f} s CPU; {len(os.sched_getaffinity(0))} host threads available"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-docs", type=int, default=-1,
+                    help="oracle baseline sample: first N documents (-1 = the whole bank, 0 = skip)")
+    ap.add_argument("--bank-tokens", type=int, default=None, help="smaller bank for a quick look (not the metric)")
+    ap.add_argument("--slab-tokens", type=int, default=8_000_000)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the bank would shard by whole documents across GPUs, see DESIGN.md.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from synth import device as sdev, workloads as W
+    from long_context_memory_msa_amd import _lib as L, memory as M, offline
+
+    dev = torch.device("cuda:0")
+    w = W.make_workload(3, bank_tokens=args.bank_tokens)
+    print(f"[bench] {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr, flush=True)
+
+    # ---- queries (host-generated, uploaded) and the pooled bank (device) -------
+    qi = W.query_inputs(w)
+    uhat = torch.from_numpy(W.gold_uhat(w, qi["QR"])).to(dev)
+    td = M.TORCH_DTYPE[w.dtype]
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(td).contiguous()
+
+    QR = up(qi["QR"][:, w.L_loc - w.T_route:w.L_loc])
+    Q = up(qi["Q"][:, w.L_loc - w.T:w.L_loc])
+    Kl = up(qi["K_loc"][:, :w.L_loc])
+    Vl = up(qi["V_loc"][:, :w.L_loc])
+    bank = M.Bank(w.doc_lens, w.chunk, w.h_kv, w.d, w.h_r, w.d_r, w.dtype, dev)
+    rope = M.Rope(w.max_pos, w.d, w.rope_base, dev)
+    t0 = time.perf_counter()
+    enc = offline.encode_bank(bank, rope, lambda a, b, K, V, KR: sdev.fill_raw_slab(w, 0, a, b, K, V, KR, uhat),
+                              args.slab_tokens, w.h_kv, w.d, w.h_r, w.d_r, time_slabs=True)
+    esz = 2 if w.dtype == "bf16" else 4
+    pooled_bytes = w.n_chunks * ((2 * w.h_kv * w.d + w.h_r * w.d_r) * esz + 4 * w.h_r + 4)
+    pool_s = sum(enc["seconds"])
+    pool_gbs = (sum(enc["raw_bytes"]) + pooled_bytes) / pool_s / 1e9
+    print(f"[bench] bank encoded in {time.perf_counter() - t0:.1f} s ({enc['slabs']} slabs, pool kernels "
+          f"{pool_s * 1e3:.1f} ms, {pool_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    O_ = torch.empty((w.n_q, w.T, w.h_q, w.d), dtype=td, device=dev)
+    idx = torch.empty((w.n_q, w.k), dtype=torch.int32, device=dev)
+    val = torch.empty((w.n_q, w.k), dtype=torch.float32, device=dev)
+    nb = L.msa_layer_workspace_bytes(bank.c, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k)
+    ws = M.workspace(nb, dev)
+    scale = L.default_scale(w.d)
+
+    def step(events=None):
+        L.msa_layer_forward(bank.c, Q, Kl, Vl, QR, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, scale,
+                            rope.c, O_, idx, val, None, ws, nb, events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = Events(4 * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev.h[4 * i:4 * i + 4])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    route = [ev.ms(ev.h[4 * i], ev.h[4 * i + 1]) for i in range(args.steps)]
+    topk = [ev.ms(ev.h[4 * i + 1], ev.h[4 * i + 2]) for i in range(args.steps)]
+    attend = [ev.ms(ev.h[4 * i + 2], ev.h[4 * i + 3]) for i in range(args.steps)]
+    layer = [ev.ms(ev.h[4 * i], ev.h[4 * i + 3]) for i in range(args.steps)]
+    ev.close()
+
+    # planted gold documents must be among each query's selection
+    gi = idx.cpu().numpy()
+    gold_ok = float(np.mean([set(w.gold[q].tolist()) <= set(gi[q].tolist()) for q in range(w.n_q)]))
+
+    ms_step = wall / args.steps * 1e3
+    route_ms = statistics.mean(route)
+    scan_bytes = w.n_chunks * (w.h_r * w.d_r * esz + 4 * w.h_r + 4)   # K^R rows + inverse norms + chunk->doc
+    achieved = scan_bytes / (route_ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": w.n_tok / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": ("100M-token memory bank, one routed layer, decode: 16 queries x 1 token, k=16, "
+                                "docs U[512,8192], chunk 128, 8 router heads x 128, 32 q / 8 KV heads x 128"),
+                   "bank_tokens": w.n_tok, "n_docs": w.n_docs, "n_chunks": w.n_chunks, "queries": w.n_q,
+                   "query_tokens": w.T, "k": w.k, "chunk": w.chunk},
+        "layer_latency_ms": statistics.median(layer),
+        "stage_ms": {"route": statistics.median(route), "topk": statistics.median(topk),
+                     "attend": statistics.median(attend)},
+        "route_tokens_per_s": w.n_tok / (route_ms * 1e-3),
+        "roofline": {"bound": "hbm", "kernel": "route_scan", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": scan_bytes},
+        "pool": {"slabs": enc["slabs"], "GB/s": pool_gbs, "frac": pool_gbs / HBM_PEAK_GBS},
+        "gold_recovered": gold_ok,
+    }
+    if args.cpu_docs != 0:
+        print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, qi, args.cpu_docs)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
