@@ -15,7 +15,6 @@ top-k, sparse attention (plus split merge).  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import ctypes
 import json
 import os
 import resource
@@ -31,36 +30,26 @@ METRIC = "memory tokens routed/sec/GPU + MSA layer latency @100M-token bank; % H
 HBM_PEAK_GBS = 8000.0
 
 
-def _hip():
-    lib = ctypes.CDLL("libamdhip64.so")
-    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    return lib
-
-
 class Events:
-    """Raw hipEvent_t handles (timing enabled) for msa_layer_forward's stage_events."""
+    """Timing events for msa_layer_forward's stage_events: torch's own events, so
+    they belong to the same HIP runtime as the stream the library launches on.
+    ``h`` holds the raw hipEvent_t handles."""
 
     def __init__(self, n: int):
-        self.hip = _hip()
-        self.h = []
-        for _ in range(n):
-            e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            self.h.append(e.value)
+        import torch
+
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.ev:          # materialise the underlying hipEvent_t
+            e.record()
+        torch.cuda.synchronize()
+        self.h = [e.cuda_event for e in self.ev]
+        self._by_handle = dict(zip(self.h, self.ev))
 
     def ms(self, a: int, b: int) -> float:
-        out = ctypes.c_float()
-        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return out.value
+        return self._by_handle[a].elapsed_time(self._by_handle[b])
 
     def close(self):
-        for e in self.h:
-            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.ev = []
 
 
 def cpu_baseline(w, qi, n_docs: int) -> dict:

@@ -144,6 +144,9 @@ int msa_rope_table(float *cos, float *sin, int32_t max_pos, int32_t d, double ba
 int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void *KR, int32_t doc_begin,
                     int32_t doc_end, const msa_rope *rope, void *stream);
 
+/* Workspace bytes msa_route_score needs for these sizes (0 = none; 0 on invalid sizes). */
+size_t msa_route_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t t_r);
+
 /*
  * Router scan with the document reduction ([LH] Component 1, key formula:
  * S = max over query tokens of the head-mean of cos(Q^R_t,h, Kbar^R_ij,h);
@@ -152,11 +155,12 @@ int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void 
  *   s_doc[q][i]   = max over the chunks c of document i of s_chunk[q][c]
  * (the document score is the max over its chunks; cosine 0 for a zero norm).
  * qr: [n_q][t_r][h_r][d_r] bank dtype; s_doc: [n_q][n_docs] fp32;
- * s_chunk: [n_q][n_chunks] fp32 or NULL.  Errors: MSA_ERR_ARG,
- * MSA_ERR_UNSUPPORTED.
+ * s_chunk: [n_q][n_chunks] fp32 or NULL; ws: msa_route_workspace_bytes bytes
+ * (16-byte aligned; may be NULL when that is 0).  Errors: MSA_ERR_ARG,
+ * MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE.
  */
 int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *s_doc, float *s_chunk,
-                    void *stream);
+                    void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes msa_topk needs for these sizes (0 on invalid sizes). */
 size_t msa_topk_workspace_bytes(int32_t n_q, int32_t n_docs, int32_t k);
@@ -206,8 +210,9 @@ size_t msa_layer_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int3
  * query tokens, all on `stream` with no host synchronisation.
  * idx [n_q][k] int32, val [n_q][k] fp32 and O are outputs; s_doc
  * [n_q][n_docs] fp32 is an optional output (NULL to skip).
- * stage_events: NULL, or 4 hipEvent_t (as void*) recorded on `stream` before
- * the scan, after the scan, after the top-k and after the attention.
+ * stage_events: NULL, or 4 hipEvent_t (as void*) recorded on `stream` just
+ * before and just after the router-scan kernel, after the top-k (which
+ * includes any per-document resolve step) and after the attention.
  * Errors: as the three calls, plus MSA_ERR_WORKSPACE.
  */
 int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,

@@ -8,13 +8,15 @@ from __future__ import annotations
 
 import ctypes
 import math
+import os
 from pathlib import Path
 from typing import Optional, Sequence
 
 import numpy as np
 
 _HERE = Path(__file__).resolve().parent
-LIB_PATH = _HERE / "libmsa.so"
+# MSA_LIBRARY selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = Path(os.environ["MSA_LIBRARY"]) if os.environ.get("MSA_LIBRARY") else _HERE / "libmsa.so"
 
 MSA_OK, MSA_ERR_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(5)
 MSA_F32, MSA_BF16 = 0, 1
@@ -43,6 +45,10 @@ class MsaBank(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime: load it first so that libmsa binds to the
+    # same runtime instance as torch's streams and allocations (one runtime per
+    # process; a second copy would not see torch's streams).
+    import torch  # noqa: F401
     if not LIB_PATH.exists():
         from . import build as _build
         _build.build()
@@ -55,7 +61,8 @@ def _load():
         "msa_bank_layout": ([P, I32, I32, P, P, P, P, P], ctypes.c_int),
         "msa_rope_table": ([P, P, I32, I32, D, P], ctypes.c_int),
         "msa_pool_memory": ([bank_p, P, P, P, I32, I32, rope_p, P], ctypes.c_int),
-        "msa_route_score": ([bank_p, P, I32, I32, P, P, P], ctypes.c_int),
+        "msa_route_workspace_bytes": ([bank_p, I32, I32], SZ),
+        "msa_route_score": ([bank_p, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
         "msa_topk_workspace_bytes": ([I32, I32, I32], SZ),
         "msa_topk": ([P, I32, I32, I32, P, P, P, SZ, P], ctypes.c_int),
         "msa_attend_workspace_bytes": ([bank_p, I32, I32, I32, I32, I32], SZ),
@@ -128,9 +135,14 @@ def msa_pool_memory(bank: MsaBank, K, V, KR, doc_begin: int, doc_end: int, rope:
                                 ctypes.byref(rope), _stream(stream)))
 
 
-def msa_route_score(bank: MsaBank, QR, n_q: int, t_r: int, s_doc, s_chunk=None, stream=None) -> None:
-    _check(_lib.msa_route_score(ctypes.byref(bank), _ptr(QR), n_q, t_r, _ptr(s_doc), _ptr(s_chunk),
-                                _stream(stream)))
+def msa_route_workspace_bytes(bank: MsaBank, n_q: int, t_r: int) -> int:
+    return _lib.msa_route_workspace_bytes(ctypes.byref(bank), n_q, t_r)
+
+
+def msa_route_score(bank: MsaBank, QR, n_q: int, t_r: int, s_doc, s_chunk=None, ws=None, ws_bytes: int = 0,
+                    stream=None) -> None:
+    _check(_lib.msa_route_score(ctypes.byref(bank), _ptr(QR), n_q, t_r, _ptr(s_doc), _ptr(s_chunk), _ptr(ws),
+                                ws_bytes, _stream(stream)))
 
 
 def msa_topk_workspace_bytes(n_q: int, n_docs: int, k: int) -> int:

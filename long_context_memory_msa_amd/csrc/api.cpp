@@ -68,7 +68,7 @@ int check_bank(const msa_bank *b) {
   CHECK_PTR(b->kbar, 16, "bank.kbar");
   CHECK_PTR(b->vbar, 16, "bank.vbar");
   CHECK_PTR(b->krbar, 16, "bank.krbar");
-  CHECK_PTR(b->kr_inv_norm, 4, "bank.kr_inv_norm");
+  CHECK_PTR(b->kr_inv_norm, 16, "bank.kr_inv_norm");
   return MSA_OK;
 }
 
@@ -131,9 +131,12 @@ msa::AttendArgs attend_args(const msa_bank *b, const void *Q, const void *K_loc,
   return a;
 }
 
-msa::RouteArgs route_args(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, uint32_t *doc_keys,
-                          uint32_t *chunk_keys) {
+msa::RouteArgs route_args(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *edges,
+                          float *doc_scores, uint32_t *doc_keys, uint32_t *chunk_out) {
   msa::RouteArgs a;
+  a.doc_chunk_off = b->doc_chunk_off;
+  a.edges = edges;
+  a.doc_scores = doc_scores;
   a.dtype = b->dtype;
   a.h_r = b->h_r;
   a.d_r = b->d_r;
@@ -146,7 +149,7 @@ msa::RouteArgs route_args(const msa_bank *b, const void *qr, int32_t n_q, int32_
   a.n_q = n_q;
   a.t_r = t_r;
   a.doc_keys = doc_keys;
-  a.chunk_keys = chunk_keys;
+  a.chunk_out = chunk_out;
   return a;
 }
 
@@ -157,11 +160,19 @@ int check_route_args(const void *qr, int32_t n_q, int32_t t_r) {
   return MSA_OK;
 }
 
-size_t layer_ws(const msa_bank *b, int32_t n_q, int32_t T, int32_t L_loc, int32_t h_q, int32_t k) {
-  const size_t keys = align_up((size_t)n_q * b->n_docs * sizeof(uint32_t));
-  const size_t tk = align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
+// layer workspace: [document scores or keys][route records][top-k candidates][attention partials]
+struct LayerWs {
+  size_t scores, route, topk, attend, total;
+};
+LayerWs layer_ws(const msa_bank *b, int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k) {
+  LayerWs w;
+  w.scores = align_up((size_t)n_q * b->n_docs * sizeof(uint32_t));
+  w.route = align_up(msa::route_ws_bytes(b->n_chunks, n_q, t_r));
+  w.topk = align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
   msa::AttendArgs a = attend_args(b, nullptr, nullptr, nullptr, n_q, T, L_loc, h_q, nullptr, k, 0, 1.f, nullptr, nullptr);
-  return keys + tk + align_up(msa::attend_ws_bytes(a));
+  w.attend = align_up(msa::attend_ws_bytes(a));
+  w.total = w.scores + w.route + w.topk + w.attend;
+  return w;
 }
 
 }  // namespace
@@ -283,8 +294,13 @@ int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void 
   }
 }
 
+size_t msa_route_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t t_r) {
+  if (!b || n_q < 1 || t_r < 1 || b->n_chunks < 1) return 0;
+  return msa::route_ws_bytes(b->n_chunks, n_q, t_r);
+}
+
 int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *s_doc, float *s_chunk,
-                    void *stream) {
+                    void *ws, size_t ws_bytes, void *stream) {
   try {
     int rc = check_bank(b);
     if (rc) return rc;
@@ -292,15 +308,25 @@ int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r,
     if (rc) return rc;
     CHECK_PTR(s_doc, 4, "s_doc");
     if (s_chunk && !aligned(s_chunk, 4)) return fail(MSA_ERR_ARG, "s_chunk is not 4-byte aligned");
+    const size_t need = msa::route_ws_bytes(b->n_chunks, n_q, t_r);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 16)))
+      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
     hipStream_t s = (hipStream_t)stream;
     const size_t nd = (size_t)n_q * b->n_docs, nc = (size_t)n_q * b->n_chunks;
-    uint32_t *dk = reinterpret_cast<uint32_t *>(s_doc);
     uint32_t *ck = reinterpret_cast<uint32_t *>(s_chunk);
-    hipError_t e = msa::launch_fill_u32(dk, nd, 0u, s);
-    if (e == hipSuccess && ck) e = msa::launch_fill_u32(ck, nc, 0u, s);
-    if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, qr, n_q, t_r, dk, ck), s);
-    if (e == hipSuccess) e = msa::launch_keys_to_scores(dk, nd, s);
-    if (e == hipSuccess && ck) e = msa::launch_keys_to_scores(ck, nc, s);
+    hipError_t e;
+    if (msa::route_single_writer(t_r)) {
+      msa::RouteArgs a = route_args(b, qr, n_q, t_r, static_cast<float *>(ws), s_doc, nullptr, ck);
+      e = msa::launch_route_scan(a, s);
+      if (e == hipSuccess) e = msa::launch_resolve_docs(a, s);
+    } else {
+      uint32_t *dk = reinterpret_cast<uint32_t *>(s_doc);
+      e = msa::launch_fill_u32(dk, nd, 0u, s);
+      if (e == hipSuccess && ck) e = msa::launch_fill_u32(ck, nc, 0u, s);
+      if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, qr, n_q, t_r, nullptr, nullptr, dk, ck), s);
+      if (e == hipSuccess) e = msa::launch_keys_to_scores(dk, nd, s);
+      if (e == hipSuccess && ck) e = msa::launch_keys_to_scores(ck, nc, s);
+    }
     return e == hipSuccess ? ok() : dev_fail(e, "route_score");
   } catch (...) {
     return fail(MSA_ERR_DEVICE, "internal error");
@@ -364,7 +390,7 @@ size_t msa_layer_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int3
   if (!b || n_q < 1 || T < 1 || t_r < 1 || L_loc < T || b->n_docs < 1 || b->h_kv < 1 || h_q < b->h_kv ||
       h_q % b->h_kv || k < 1 || k > b->n_docs || k > 256 || (b->d != 64 && b->d != 128))
     return 0;
-  return layer_ws(b, n_q, T, L_loc, h_q, k);
+  return layer_ws(b, n_q, T, t_r, L_loc, h_q, k).total;
 }
 
 int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,
@@ -385,31 +411,45 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
     if (stage_events)
       for (int i = 0; i < 4; ++i)
         if (!stage_events[i]) return fail(MSA_ERR_ARG, "stage_events[%d] is null", i);
-    const size_t need = layer_ws(b, n_q, T, L_loc, h_q, k);
-    if (!ws || ws_bytes < need || !aligned(ws, 256))
-      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", need, ws_bytes);
+    const LayerWs lw = layer_ws(b, n_q, T, t_r, L_loc, h_q, k);
+    if (!ws || ws_bytes < lw.total || !aligned(ws, 256))
+      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", lw.total, ws_bytes);
     hipStream_t s = (hipStream_t)stream;
     char *w = static_cast<char *>(ws);
-    uint32_t *keys = reinterpret_cast<uint32_t *>(w);
+    void *rt_ws = w + lw.scores;
+    void *tk_ws = static_cast<char *>(rt_ws) + lw.route;
+    void *at_ws = static_cast<char *>(tk_ws) + lw.topk;
     const size_t nd = (size_t)n_q * b->n_docs;
-    void *tk_ws = w + align_up(nd * sizeof(uint32_t));
-    void *at_ws = static_cast<char *>(tk_ws) + align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
     auto rec = [&](int i) -> hipError_t {
       return stage_events ? hipEventRecord((hipEvent_t)stage_events[i], s) : hipSuccess;
     };
-    hipError_t e = msa::launch_fill_u32(keys, nd, 0u, s);
-    if (e == hipSuccess) e = rec(0);
-    if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, QR, n_q, t_r, keys, nullptr), s);
-    if (e == hipSuccess) e = rec(1);
-    if (e == hipSuccess) e = msa::launch_topk(nullptr, keys, n_q, b->n_docs, k, idx, val, tk_ws, s);
-    if (e == hipSuccess) e = rec(2);
+    hipError_t e = hipSuccess;
+    if (msa::route_single_writer(t_r)) {
+      // scores written once per document: no zero fill, no keys
+      float *scores = s_doc ? s_doc : reinterpret_cast<float *>(w);
+      msa::RouteArgs ra = route_args(b, QR, n_q, t_r, static_cast<float *>(rt_ws), scores, nullptr, nullptr);
+      e = rec(0);
+      if (e == hipSuccess) e = msa::launch_route_scan(ra, s);
+      if (e == hipSuccess) e = rec(1);
+      if (e == hipSuccess) e = msa::launch_resolve_docs(ra, s);
+      if (e == hipSuccess) e = msa::launch_topk(scores, nullptr, n_q, b->n_docs, k, idx, val, tk_ws, s);
+      if (e == hipSuccess) e = rec(2);
+    } else {
+      uint32_t *keys = reinterpret_cast<uint32_t *>(w);
+      e = msa::launch_fill_u32(keys, nd, 0u, s);
+      if (e == hipSuccess) e = rec(0);
+      if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, QR, n_q, t_r, nullptr, nullptr, keys, nullptr), s);
+      if (e == hipSuccess) e = rec(1);
+      if (e == hipSuccess) e = msa::launch_topk(nullptr, keys, n_q, b->n_docs, k, idx, val, tk_ws, s);
+      if (e == hipSuccess) e = rec(2);
+      if (e == hipSuccess && s_doc) {
+        e = hipMemcpyAsync(s_doc, keys, nd * sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess) e = msa::launch_keys_to_scores(reinterpret_cast<uint32_t *>(s_doc), nd, s);
+      }
+    }
     if (e == hipSuccess)
       e = msa::launch_attend(attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, idx, k, pos0, scale, rope, O), at_ws, s);
     if (e == hipSuccess) e = rec(3);
-    if (e == hipSuccess && s_doc) {
-      e = hipMemcpyAsync(s_doc, keys, nd * sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
-      if (e == hipSuccess) e = msa::launch_keys_to_scores(reinterpret_cast<uint32_t *>(s_doc), nd, s);
-    }
     return e == hipSuccess ? ok() : dev_fail(e, "layer_forward");
   } catch (...) {
     return fail(MSA_ERR_DEVICE, "internal error");

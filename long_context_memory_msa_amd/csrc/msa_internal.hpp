@@ -38,11 +38,20 @@ struct RouteArgs {
   const void *krbar;
   const float *kr_inv_norm;
   const int32_t *chunk_doc;
+  const int64_t *doc_chunk_off;  // device [n_docs+1]
   const void *qr;                // [n_q][t_r][h_r][d_r]
   int n_q, t_r;
-  uint32_t *doc_keys;            // [n_q][n_docs], zeroed before the scan
-  uint32_t *chunk_keys;          // [n_q][n_chunks] or null, zeroed before the scan
+  // single-writer mode (edges != null): fp32 scores written directly
+  float *edges;                  // [row blocks][tiles][2][16] per-tile segment records
+  float *doc_scores;             // [n_q][n_docs] fp32
+  // atomic mode (edges == null): order-preserving keys, zeroed before the scan
+  uint32_t *doc_keys;            // [n_q][n_docs]
+  // optional per-chunk scores [n_q][n_chunks]: fp32 in single-writer mode, keys otherwise
+  uint32_t *chunk_out;
 };
+bool route_single_writer(int t_r);                    // (query, document) scores have one writer
+size_t route_ws_bytes(int64_t n_chunks, int n_q, int t_r);
+hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);
 hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s);  // in place

@@ -16,16 +16,59 @@
 //    dot * invQ[row,h] * invK[c,h] summed over heads, so no normalised bf16
 //    copy of either side is made;
 //  * max over the query tokens of a query runs across the lanes of the tile,
-//    then a segmented max over each run of chunks of one document, and one
-//    order-preserving atomicMax per (query, document run) into the scores;
-//  * persistent waves each own a contiguous range of chunk tiles.
+//    then a segmented max-scan over the runs of chunks that belong to one
+//    document;
+//  * persistent waves take tiles in an interleaved order (wave w: tiles w,
+//    w + W, ...), so the waves stream one compact window of the bank;
+//  * when every (query, document) score has a single writer (one query per
+//    row, or one row block per query) a tile emits one coalesced 128-byte
+//    record with the max of its first and of its last document segment per
+//    query, documents lying strictly inside the tile are stored directly, and
+//    a small second kernel resolves each document from the records of the
+//    tiles it spans -- no atomics and no zero fill; otherwise each segment
+//    goes out as an order-preserving atomicMax on uint32 keys.
 #include <algorithm>
 
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
+// Tuning knobs (compile-time): prefetch depth in heads, and whether the key
+// stream uses non-temporal loads.
+#ifndef MSA_ROUTE_PD
+#define MSA_ROUTE_PD 2
+#endif
+#ifndef MSA_ROUTE_NT
+#define MSA_ROUTE_NT 0
+#endif
+// workgroups per CU in the persistent grid (0 = as many as stay resident)
+#ifndef MSA_ROUTE_WGCU
+#define MSA_ROUTE_WGCU 0
+#endif
+// 1 = query fragments held in VGPRs, 0 = re-read from LDS each step
+#ifndef MSA_ROUTE_QREG
+#define MSA_ROUTE_QREG 0
+#endif
+#ifndef MSA_ROUTE_WAVES
+#define MSA_ROUTE_WAVES 3
+#endif
+
 namespace msa {
 namespace {
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type load_stream(const T *p) {
+#if MSA_ROUTE_NT
+  if constexpr (sizeof(T) == 2) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    return __builtin_nontemporal_load(p);
+  }
+#else
+  return load_frag<T>(p);
+#endif
+}
 
 __global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
@@ -36,21 +79,21 @@ __global__ void keys_to_scores_kernel(uint32_t *p, size_t n) {
     p[i] = __float_as_uint(key_score(p[i]));
 }
 
-// Segmented max over the 16 columns of a lane group: columns hold chunks in
-// bank order, `doc` their documents (-1 = no chunk).  Returns, in the first
-// lane of each run of equal doc, the max over the run.
-__device__ __forceinline__ float seg_max16(float v, int doc, int col) {
+// Inclusive max-scan within runs of equal document over the 16 columns of a
+// lane group (columns hold consecutive chunks); match[j] says whether column
+// col - 2^j holds the same document.  The last column of a run then holds
+// the run's max.
+__device__ __forceinline__ float seg_scan16(float v, const bool (&match)[4]) {
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    float nv = __shfl_down(v, o, 16);
-    int nd = __shfl_down(doc, o, 16);
-    if (col + o < 16 && nd == doc) v = fmaxf(v, nv);
+  for (int j = 0; j < 4; ++j) {
+    const float nv = __shfl_up(v, 1 << j, 16);
+    if (match[j]) v = fmaxf(v, nv);
   }
   return v;
 }
 
-template <typename T, int HR, int DR>
-__global__ __launch_bounds__(256, 3) void route_scan_kernel(RouteArgs a, int64_t n_tiles, int tiles_per_wave) {
+template <typename T, int HR, int DR, bool EDGE>
+__global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteArgs a, int64_t n_tiles, int64_t n_waves) {
   using F = Frag<T>;
   using FT = typename F::type;
   constexpr int EL = F::EL, KW = F::KW, KS = DR / KW, NF = HR * KS;
@@ -98,128 +141,229 @@ __global__ __launch_bounds__(256, 3) void route_scan_kernel(RouteArgs a, int64_t
     const int row = rb * 16 + 4 * G + i;
     rowq[i] = row < n_rows ? row / a.t_r : -1;
   }
+  // interleaved tile order: at any moment the waves stream one compact window
   const int64_t wave_id = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t t_lo = wave_id * tiles_per_wave;
-  const int64_t t_hi = t_lo + tiles_per_wave < n_tiles ? t_lo + tiles_per_wave : n_tiles;
+  const int64_t t_lo = wave_id, t_hi = n_tiles, t_step = n_waves;
   const T *krbar = static_cast<const T *>(a.krbar);
 
   // Prefetch ring: the key fragments of PD (tile, head) steps are in flight
   // while the MFMAs of the current step run; it streams across tile ends.
-  constexpr int PD = HR < 4 ? HR : 4;
+  // Inverse norms and document ids of the next tile are fetched one tile ahead.
+  constexpr int PD = HR < MSA_ROUTE_PD ? HR : MSA_ROUTE_PD;
   FT ring[PD][KS];
-  float ring_ik[PD];
+  float ik_cur[HR], ik_nxt[HR];
+  int doc_cur = -1, doc_nxt = -1;
   auto lane_chunk = [&](int64_t tl) -> int64_t {
     const int64_t cp = tl * 16 + col;
     return cp < a.n_chunks ? cp : a.n_chunks - 1;
   };
-  int64_t c_nxt = lane_chunk(t_lo);
-  const T *kp_nxt = krbar + c_nxt * (HR * DR) + G * EL;
-  const float *ik_nxt = a.kr_inv_norm + c_nxt * HR;
-  const T *kp_cur = kp_nxt;
-  const float *ik_cur = ik_nxt;
+  auto load_meta = [&](int64_t tl, float (&ik)[HR], int &doc) {
+    const int64_t cp = lane_chunk(tl);
+    const float *ip = a.kr_inv_norm + cp * HR;
+    if constexpr (HR % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < HR / 4; ++j) {
+        const float4 v = reinterpret_cast<const float4 *>(ip)[j];
+        ik[4 * j] = v.x; ik[4 * j + 1] = v.y; ik[4 * j + 2] = v.z; ik[4 * j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < HR; ++j) ik[j] = ip[j];
+    }
+    doc = (tl * 16 + col < a.n_chunks) ? a.chunk_doc[cp] : -1;
+  };
+#if MSA_ROUTE_QREG
+  FT qreg[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) qreg[f] = qfrag[f][lane];
+#define MSA_QOP(f) qreg[f]
+#else
+#define MSA_QOP(f) qfrag[(f) + zoff][lane]
+#endif
+  const T *kp_cur = krbar + lane_chunk(t_lo) * (HR * DR) + G * EL;
+  const T *kp_nxt = kp_cur;
   if (t_lo < t_hi) {
 #pragma unroll
-    for (int p = 0; p < PD; ++p) {
+    for (int p = 0; p < PD; ++p)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) ring[p][s] = load_frag<T>(kp_cur + p * DR + s * KW);
-      ring_ik[p] = ik_cur[p];
-    }
+      for (int s = 0; s < KS; ++s) ring[p][s] = load_stream<T>(kp_cur + p * DR + s * KW);
+    load_meta(t_lo, ik_cur, doc_cur);
   }
 
-  for (int64_t tile = t_lo; tile < t_hi; ++tile) {
+  for (int64_t tile = t_lo; tile < t_hi; tile += t_step) {
+    const int64_t tile_next = tile + t_step;
     const int64_t c = tile * 16 + col;
     const bool cv = c < a.n_chunks;
-    const int64_t cc = cv ? c : a.n_chunks - 1;
-    kp_cur = kp_nxt;
-    ik_cur = ik_nxt;
-    const bool more = tile + 1 < t_hi;
+    const bool more = tile_next < t_hi;
     if (more) {
-      c_nxt = lane_chunk(tile + 1);
-      kp_nxt = krbar + c_nxt * (HR * DR) + G * EL;
-      ik_nxt = a.kr_inv_norm + c_nxt * HR;
+      kp_nxt = krbar + lane_chunk(tile_next) * (HR * DR) + G * EL;
+      load_meta(tile_next, ik_nxt, doc_nxt);
     }
-    const int doc = cv ? a.chunk_doc[cc] : -1;
+#if !MSA_ROUTE_QREG
     // opaque zero: keeps the query-fragment LDS reads inside the loop rather
     // than hoisting all of Q into VGPRs (registers go to the prefetch ring)
     int zoff;
     asm volatile("s_mov_b32 %0, 0" : "=s"(zoff));
+#endif
     f32x4 S = zero4();
-    // heads in groups of PD; slot p of the ring holds head hg + p
-#pragma unroll 1
-    for (int hg = 0; hg < HR; hg += PD) {
 #pragma unroll
-      for (int p = 0; p < PD; ++p) {
-        const int h = hg + p;
-        f32x4 acc = zero4();
+    for (int h = 0; h < HR; ++h) {
+      const int slot = h % PD;
+      f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma16(qfrag[h * KS + s + zoff][lane], ring[p][s], acc);
-        const float ik = ring_ik[p];
-        const float4 iq = *reinterpret_cast<const float4 *>(&qinv[h][4 * G]);
-        S[0] += acc[0] * (iq.x * ik);
-        S[1] += acc[1] * (iq.y * ik);
-        S[2] += acc[2] * (iq.z * ik);
-        S[3] += acc[3] * (iq.w * ik);
-        if (hg + PD < HR) {
+      for (int s = 0; s < KS; ++s) acc = mfma16(MSA_QOP(h * KS + s), ring[slot][s], acc);
+      const float ik = ik_cur[h];
+      const float4 iq = *reinterpret_cast<const float4 *>(&qinv[h][4 * G]);
+      S[0] += acc[0] * (iq.x * ik);
+      S[1] += acc[1] * (iq.y * ik);
+      S[2] += acc[2] * (iq.z * ik);
+      S[3] += acc[3] * (iq.w * ik);
+      if (h + PD < HR) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) ring[p][s] = load_frag<T>(kp_cur + (h + PD) * DR + s * KW);
-          ring_ik[p] = ik_cur[h + PD];
-        } else if (more) {
+        for (int s = 0; s < KS; ++s) ring[slot][s] = load_stream<T>(kp_cur + (h + PD) * DR + s * KW);
+      } else if (more) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) ring[p][s] = load_frag<T>(kp_nxt + (h + PD - HR) * DR + s * KW);
-          ring_ik[p] = ik_nxt[h + PD - HR];
-        }
+        for (int s = 0; s < KS; ++s) ring[slot][s] = load_stream<T>(kp_nxt + (h + PD - HR) * DR + s * KW);
       }
+      // keep the head steps in order: later heads' loads are not hoisted above this one
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const int prev_doc = __shfl_up(doc, 1, 16);
-    const bool head = (col == 0) || (prev_doc != doc);
+#undef MSA_QOP
+    const int doc = doc_cur;
+    kp_cur = kp_nxt;
+#pragma unroll
+    for (int j = 0; j < HR; ++j) ik_cur[j] = ik_nxt[j];
+    doc_cur = doc_nxt;
+    // ---- epilogue: token max, then per-document max over runs of columns ----
+    // (cross-lane reads are made by every lane: a lane that skips a shuffle
+    // leaves its value undefined for the lanes that read it)
+    const int d0 = __shfl(doc, 0, 16), d15 = __shfl(doc, 15, 16);
+    const int doc_right = __shfl_down(doc, 1, 16);
+    const bool tail = (col == 15) || (doc_right != doc);
+    bool match[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int doc_left = __shfl_up(doc, 1 << j, 16);
+      match[j] = col >= (1 << j) && doc_left == doc;
+    }
+    // last column holding the tile's first document (documents are contiguous)
+    const unsigned long long same0 = __ballot(doc == d0);
+    const int tail0 = __popcll((same0 >> (16 * G)) & 0xFFFFull) - 1;
+    float *erec = EDGE ? a.edges + (rb * n_tiles + tile) * 32 : nullptr;  // [2][16] floats
     if (uniform) {
-      // every row of the block belongs to query rowq[0]: max over the 16 rows
+      // every row of the block belongs to one query: max over the 16 rows first
       float v = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
       v = fmaxf(v, __shfl_xor(v, 16, 64));
       v = fmaxf(v, __shfl_xor(v, 32, 64));
       const int q = rb * 16 / a.t_r;
-      if (a.chunk_keys && G == 0 && cv) atomicMax(a.chunk_keys + (int64_t)q * a.n_chunks + c, score_key(v));
-      v = seg_max16(v, doc, col);
-      if (G == 0 && head && doc >= 0) atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(v));
+      if (a.chunk_out && G == 0 && cv) {
+        if constexpr (EDGE) reinterpret_cast<float *>(a.chunk_out)[(int64_t)q * a.n_chunks + c] = v;
+        else atomicMax(a.chunk_out + (int64_t)q * a.n_chunks + c, score_key(v));
+      }
+      v = seg_scan16(cv ? v : -INFINITY, match);
+      if constexpr (EDGE) {
+        const float first = __shfl(v, tail0, 16), last = __shfl(v, 15, 16);
+        if (G == 0 && tail && doc >= 0 && doc != d0 && doc != d15) a.doc_scores[(int64_t)q * a.n_docs + doc] = v;
+        if (G == 0 && col < 2) erec[col * 16] = col == 0 ? first : last;
+      } else {
+        if (G == 0 && tail && doc >= 0) atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(v));
+      }
     } else {
+      float first[4], last[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const int q = rowq[i];
         float v = S[i];
-        if (a.chunk_keys && cv && rowq[i] >= 0)
-          atomicMax(a.chunk_keys + (int64_t)rowq[i] * a.n_chunks + c, score_key(v));
-        v = seg_max16(v, doc, col);
-        if (head && doc >= 0 && rowq[i] >= 0) atomicMax(a.doc_keys + (int64_t)rowq[i] * a.n_docs + doc, score_key(v));
+        if (a.chunk_out && cv && q >= 0) {
+          if constexpr (EDGE) reinterpret_cast<float *>(a.chunk_out)[(int64_t)q * a.n_chunks + c] = v;
+          else atomicMax(a.chunk_out + (int64_t)q * a.n_chunks + c, score_key(v));
+        }
+        v = seg_scan16(cv ? v : -INFINITY, match);
+        if constexpr (EDGE) {
+          first[i] = __shfl(v, tail0, 16);
+          last[i] = __shfl(v, 15, 16);
+          if (tail && doc >= 0 && doc != d0 && doc != d15 && q >= 0) a.doc_scores[(int64_t)q * a.n_docs + doc] = v;
+        } else {
+          if (tail && doc >= 0 && q >= 0) atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(v));
+        }
+      }
+      if constexpr (EDGE) {
+        // one 128-byte record per tile: lanes (G, col 0) write the first-segment maxima
+        // of rows 4G..4G+3, lanes (G, col 1) the last-segment maxima
+        if (col < 2) {
+          const float *src = col == 0 ? first : last;
+          *reinterpret_cast<float4 *>(erec + col * 16 + 4 * G) = float4{src[0], src[1], src[2], src[3]};
+        }
       }
     }
   }
 }
 
-template <typename T, int HR, int DR>
+// Document scores from the per-tile records (single-writer mode): a document
+// spanning tiles ta..tb is the last segment of ta and the first segment of
+// every later tile it reaches; a document strictly inside one tile was
+// stored by the scan itself.
+__global__ void resolve_docs_kernel(const float *edges, const int64_t *doc_chunk_off, int n_q, int n_docs,
+                                    int64_t n_tiles, int t_r, float *doc_scores) {
+  // query fastest: the lanes of a wave read consecutive rows of the same tile records
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_q * n_docs) return;
+  const int q = (int)(i % n_q), doc = (int)(i / n_q);
+  const int rb = t_r == 1 ? q / 16 : q;          // row block of this query
+  const int r = t_r == 1 ? q % 16 : 0;           // its row within the block's records
+  const int64_t c0 = doc_chunk_off[doc], c1 = doc_chunk_off[doc + 1] - 1;
+  const int64_t ta = c0 / 16, tb = c1 / 16;
+  if (ta == tb && (c0 % 16) != 0 && (c1 % 16) != 15) return;  // interior: already stored
+  const float *rec = edges + (int64_t)rb * n_tiles * 32;
+  float v;
+  if (ta == tb) {
+    v = rec[ta * 32 + ((c0 % 16) == 0 ? 0 : 16) + r];
+  } else {
+    v = rec[ta * 32 + 16 + r];
+    for (int64_t t = ta + 1; t <= tb; ++t) v = fmaxf(v, rec[t * 32 + r]);
+  }
+  doc_scores[(int64_t)q * n_docs + doc] = v;
+}
+
+template <typename T, int HR, int DR, bool EDGE>
 hipError_t route_launch(const RouteArgs &a, hipStream_t s) {
+  // Persistent grid: exactly as many workgroups as stay resident together
+  // (occupancy of this kernel x compute units), so no second, partial round.
+  static int resident = 0;  // workgroups per CU for this instantiation
+  if (resident == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, route_scan_kernel<T, HR, DR, EDGE>, 256, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    resident = MSA_ROUTE_WGCU > 0 && MSA_ROUTE_WGCU < n ? MSA_ROUTE_WGCU : n;
+  }
   const int64_t n_tiles = (a.n_chunks + 15) / 16;
   const int n_rows = a.n_q * a.t_r;
   const int rbs = (n_rows + 15) / 16;
-  const int64_t target_waves = (int64_t)device_cu_count() * 16;
-  int64_t waves = std::max<int64_t>(4, target_waves / rbs);
-  if (waves > n_tiles) waves = n_tiles;
-  int tiles_per_wave = (int)((n_tiles + waves - 1) / waves);
-  waves = (n_tiles + tiles_per_wave - 1) / tiles_per_wave;
-  int64_t wgs = (waves + 3) / 4;
+  const int64_t slots = (int64_t)device_cu_count() * resident;  // resident workgroups
+  int64_t wgs = std::max<int64_t>(1, slots / rbs);
+  wgs = std::min<int64_t>(wgs, (n_tiles + 3) / 4);
+  const int64_t n_waves = wgs * 4;  // wave w starts at tile w
   dim3 grid((unsigned)wgs, (unsigned)rbs), block(256);
-  hipLaunchKernelGGL((route_scan_kernel<T, HR, DR>), grid, block, 0, s, a, n_tiles, tiles_per_wave);
+  hipLaunchKernelGGL((route_scan_kernel<T, HR, DR, EDGE>), grid, block, 0, s, a, n_tiles, n_waves);
   return hipGetLastError();
+}
+
+template <typename T, int HR, int DR>
+hipError_t route_mode(const RouteArgs &a, hipStream_t s) {
+  return a.edges ? route_launch<T, HR, DR, true>(a, s) : route_launch<T, HR, DR, false>(a, s);
 }
 
 template <typename T, int DR>
 hipError_t route_by_hr(const RouteArgs &a, hipStream_t s) {
   // the API admits h_r * d_r <= 1024
   switch (a.h_r) {
-    case 1: return route_launch<T, 1, DR>(a, s);
-    case 2: return route_launch<T, 2, DR>(a, s);
-    case 4: return route_launch<T, 4, DR>(a, s);
-    case 8: return route_launch<T, 8, DR>(a, s);
+    case 1: return route_mode<T, 1, DR>(a, s);
+    case 2: return route_mode<T, 2, DR>(a, s);
+    case 4: return route_mode<T, 4, DR>(a, s);
+    case 8: return route_mode<T, 8, DR>(a, s);
     default:
-      if constexpr (DR == 64) return route_launch<T, 16, DR>(a, s);
+      if constexpr (DR == 64) return route_mode<T, 16, DR>(a, s);
       return hipErrorInvalidValue;
   }
 }
@@ -237,6 +381,21 @@ hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   size_t g = std::min<size_t>((n + 255) / 256, 8192);
   hipLaunchKernelGGL(keys_to_scores_kernel, dim3((unsigned)g), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+bool route_single_writer(int t_r) { return t_r == 1 || t_r == 16; }
+
+size_t route_ws_bytes(int64_t n_chunks, int n_q, int t_r) {
+  if (!route_single_writer(t_r)) return 0;
+  const int64_t rbs = ((int64_t)n_q * t_r + 15) / 16;
+  return (size_t)rbs * ((n_chunks + 15) / 16) * 32 * sizeof(float);
+}
+
+hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_q * a.n_docs;
+  hipLaunchKernelGGL(resolve_docs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.edges,
+                     a.doc_chunk_off, a.n_q, a.n_docs, (a.n_chunks + 15) / 16, a.t_r, a.doc_scores);
   return hipGetLastError();
 }
 

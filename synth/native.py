@@ -63,6 +63,7 @@ def host_lib():
 def dev_lib():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (bind to torch's HIP runtime, loaded first)
         if not DEV_SO.exists():
             build_dev()
         lib = ctypes.CDLL(str(DEV_SO))

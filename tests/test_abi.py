@@ -96,15 +96,15 @@ def test_bank_validation():
                        ({"h_r": 3}, L.MSA_ERR_UNSUPPORTED), ({"n_docs": 0}, L.MSA_ERR_ARG),
                        ({"max_doc_chunks": 9}, L.MSA_ERR_ARG), ({"kbar": None}, L.MSA_ERR_ARG),
                        ({"krbar": MIS.addr}, L.MSA_ERR_ARG), ({"n_chunks": 1}, L.MSA_ERR_ARG)):
-        assert _code(msa.msa_route_score, _bank(**over), A, 1, 1, A, None, 0) == code, over
+        assert _code(msa.msa_route_score, _bank(**over), A, 1, 1, A, None, A, 1 << 30, stream=0) == code, over
 
 
 def test_route_validation():
-    assert _code(msa.msa_route_score, _bank(), None, 1, 1, A, None, 0) == L.MSA_ERR_ARG
-    assert _code(msa.msa_route_score, _bank(), A, 0, 1, A, None, 0) == L.MSA_ERR_ARG
-    assert _code(msa.msa_route_score, _bank(), A, 1, 0, A, None, 0) == L.MSA_ERR_ARG
-    assert _code(msa.msa_route_score, _bank(), MIS, 1, 1, A, None, 0) == L.MSA_ERR_ARG
-    assert _code(msa.msa_route_score, _bank(), A, 1, 1, None, None, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), None, 1, 1, A, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), A, 0, 1, A, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), A, 1, 0, A, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), MIS, 1, 1, A, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), A, 1, 1, None, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
 
 
 def test_topk_validation_and_workspace():

@@ -111,7 +111,8 @@ def test_pool_edge_lengths(device, dtype):
 
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name,t_r,n_q", [("cfg0", 16, 1), ("cfg1", 128, 1), ("cfg1", 1, 1), ("cfg1", 5, 3),
-                                          ("cfg1", 40, 2), ("cfg2", 256, 1), ("cfg3", 1, 16)])
+                                          ("cfg1", 40, 2), ("cfg1", 16, 3), ("cfg1", 1, 37), ("cfg2", 256, 1),
+                                          ("cfg3", 1, 16)])
 def test_route_isolated(device, name, t_r, n_q):
     cfg, bt = SMALL[name]
     w = _wl(cfg, bt)
@@ -126,13 +127,15 @@ def test_route_isolated(device, name, t_r, n_q):
     bank, _ = gpu_bank_from_oracle(w, ob, device)
     s_doc = torch.empty((n_q, w.n_docs), dtype=torch.float32, device=device)
     s_chunk = torch.empty((n_q, w.n_chunks), dtype=torch.float32, device=device)
-    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc, s_chunk)
+    nb = L.msa_route_workspace_bytes(bank.c, n_q, t_r)
+    ws = M.workspace(nb, device)
+    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc, s_chunk, ws, nb)
     torch.cuda.synchronize()
     assert np.abs(host(s_chunk) - S).max() <= 2e-3
     assert np.abs(host(s_doc) - sd).max() <= 2e-3
     # without the optional chunk output
     s_doc2 = torch.empty_like(s_doc)
-    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc2, None)
+    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc2, None, ws, nb)
     torch.cuda.synchronize()
     assert torch.equal(s_doc, s_doc2)
 
@@ -249,7 +252,9 @@ def test_layer_equals_composition_and_is_deterministic(device):
     assert torch.equal(o1, o2) and torch.equal(i1, i2) and torch.equal(v1, v2) and torch.equal(s1, s2)
     # the same three steps through the individual entry points
     s_doc = torch.empty_like(s1)
-    L.msa_route_score(bank.c, QR, w.n_q, w.T_route, s_doc, None)
+    nb0 = L.msa_route_workspace_bytes(bank.c, w.n_q, w.T_route)
+    ws0 = M.workspace(nb0, device)
+    L.msa_route_score(bank.c, QR, w.n_q, w.T_route, s_doc, None, ws0, nb0)
     idx = torch.empty_like(i1)
     val = torch.empty_like(v1)
     nb = L.msa_topk_workspace_bytes(w.n_q, w.n_docs, w.k)
