@@ -52,6 +52,28 @@ class Events:
         self.ev = []
 
 
+def route_traffic(bytes_per_launch: int):
+    """HBM bytes per router-scan launch from the committed counter passes, or None
+    when the kernel source changed since they were taken (see profiles/)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "route_scan_100M_decode_traffic.txt")
+    try:
+        kv = {}
+        for line in open(path):
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k] = v
+        src = b"".join(open(os.path.join(ROOT, "long_context_memory_msa_amd", "csrc", f), "rb").read()
+                       for f in ("route.hip", "msa_device.hpp"))
+        if hashlib.sha256(src).hexdigest()[:16] != kv["kernel_source_sha256_16"]:
+            return None
+        return (float(kv["fetch_kib"]) * float(kv["fetch_factor"]) +
+                float(kv["write_kib"]) * float(kv["write_factor"])) * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, qi, n_docs: int) -> dict:
     """The fp64 oracle's layer forward on the first ``n_docs`` documents of the
     bank (pooled-shape synthetic values; the oracle's time does not depend on
@@ -104,6 +126,8 @@ def main() -> int:
                     help="oracle baseline sample: first N documents (-1 = the whole bank, 0 = skip)")
     ap.add_argument("--bank-tokens", type=int, default=None, help="smaller bank for a quick look (not the metric)")
     ap.add_argument("--slab-tokens", type=int, default=8_000_000)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -114,6 +138,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return 0
 
     from synth import device as sdev, workloads as W
     from long_context_memory_msa_amd import _lib as L, memory as M, offline
@@ -203,7 +237,7 @@ def main() -> int:
                      "attend": statistics.median(attend)},
         "route_tokens_per_s": w.n_tok / (route_ms * 1e-3),
         "roofline": {"bound": "hbm", "kernel": "route_scan", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": route_traffic(scan_bytes),
                      "bytes_per_launch": scan_bytes},
         "pool": {"slabs": enc["slabs"], "GB/s": pool_gbs, "frac": pool_gbs / HBM_PEAK_GBS},
         "gold_recovered": gold_ok,

@@ -1,0 +1,68 @@
+"""Memory Interleave over the routed layers: rounds of route -> top-k ->
+attend, re-routing after each round of newly generated tokens (hotdry blog,
+sparse strategy: routing alternates with generation and is redone each round;
+hotdry blog, parameters: 2-3 rounds; Lighthouse digest, Component 3).
+
+Round r of layer l routes with all active tokens of the layer's context
+(T0 + append * r), then attends the tokens that are new in this round (T0 in
+round 0, ``append`` afterwards) over the selected documents plus the whole
+causal local context.  Appending is the caller's: the context tensors hold the
+whole final context and each round uses a prefix of it.  This module is a
+host loop over msa_layer_forward; all computation runs in the kernels.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from .memory import TORCH_DTYPE, Bank, Rope, workspace
+
+
+def _contig(t: torch.Tensor) -> torch.Tensor:
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def interleave(banks: Sequence[Bank], rope: Rope, layers: Sequence[Dict[str, torch.Tensor]], T0: int, append: int,
+               rounds: int, k: int, pos0: int, h_q: int, scale: Optional[float] = None,
+               want_scores: bool = False, stream=None) -> List[List[Dict[str, torch.Tensor]]]:
+    """Run ``rounds`` interleave rounds over all layers.
+
+    ``layers[l]`` holds device tensors Q [n_q][L][h_q][d], K_loc / V_loc
+    [n_q][L][h_kv][d] and QR [n_q][L][h_r][d_r] over the whole context
+    (L >= T0 + append * (rounds - 1)).  Returns out[r][l] = {O, idx, val
+    [, s_doc]}.
+    """
+    if not banks or len(banks) != len(layers):
+        raise ValueError("one bank per layer is required")
+    n_q = layers[0]["Q"].shape[0]
+    d = layers[0]["Q"].shape[-1]
+    scale = _lib.default_scale(d) if scale is None else scale
+    dev = layers[0]["Q"].device
+    td = TORCH_DTYPE[banks[0].dtype]
+    # one workspace for the largest round
+    nb = max(_lib.msa_layer_workspace_bytes(b.c, n_q, T0 if r == 0 else append, T0 + append * r, T0 + append * r,
+                                            h_q, k)
+             for b in banks for r in range(rounds))
+    ws = workspace(nb, dev)
+    out = []
+    for r in range(rounds):
+        L_act = T0 + append * r
+        T_new = T0 if r == 0 else append
+        res_r = []
+        for bank, inp in zip(banks, layers):
+            O = torch.empty((n_q, T_new, h_q, d), dtype=td, device=dev)
+            idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+            val = torch.empty((n_q, k), dtype=torch.float32, device=dev)
+            s_doc = torch.empty((n_q, bank.n_docs), dtype=torch.float32, device=dev) if want_scores else None
+            _lib.msa_layer_forward(bank.c, _contig(inp["Q"][:, L_act - T_new:L_act]),
+                                   _contig(inp["K_loc"][:, :L_act]), _contig(inp["V_loc"][:, :L_act]),
+                                   _contig(inp["QR"][:, :L_act]), n_q, T_new, L_act, L_act, h_q, k, pos0, scale,
+                                   rope.c, O, idx, val, s_doc, ws, nb, None, stream)
+            res = {"O": O, "idx": idx, "val": val}
+            if want_scores:
+                res["s_doc"] = s_doc
+            res_r.append(res)
+        out.append(res_r)
+    return out

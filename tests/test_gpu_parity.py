@@ -267,3 +267,34 @@ def test_layer_equals_composition_and_is_deterministic(device):
                         rope.c, out, ws2, nb2)
     torch.cuda.synchronize()
     assert torch.equal(s_doc, s1) and torch.equal(idx, i1) and torch.equal(val, v1) and torch.equal(out, o1)
+
+
+def test_interleave_small(device):
+    # the interleave driver on 2 layers of a small bank against the oracle's loop
+    from long_context_memory_msa_amd.interleave import interleave
+
+    w = W.make_workload(4, bank_tokens=120_000, n_layers=2)
+    banks, layers, ob_banks, hosts = [], [], [], []
+    for layer in range(w.n_layers):
+        qi = W.query_inputs(w, layer)
+        K = W.bank_raw(w, rng.ROLE_K, 0, w.n_tok, layer)
+        V = W.bank_raw(w, rng.ROLE_V, 0, w.n_tok, layer)
+        KR = W.bank_raw(w, rng.ROLE_KR, 0, w.n_tok, layer)
+        ob_banks.append(oracle_bank(w, K, V, KR))
+        bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
+        banks.append(bank)
+        hosts.append(qi)
+        layers.append({k_: dev(v, w.dtype, device) for k_, v in qi.items()})
+    res = interleave(banks, rope, layers, w.L_loc, w.append, w.rounds, w.k, w.pos0, w.h_q, want_scores=True)
+    torch.cuda.synchronize()
+    want = O.interleave(hosts, ob_banks, w.L_loc, w.append, w.rounds, w.k, w.pos0, base=w.rope_base)
+    for r in range(w.rounds):
+        for layer in range(w.n_layers):
+            g_, o_ = res[r][layer], want[r][layer]
+            assert np.abs(host(g_["s_doc"]) - o_["s_doc"]).max() <= 2e-3
+            gi = g_["idx"].cpu().numpy()
+            if o_["gap"][0] > 4e-3:
+                assert set(gi[0].tolist()) == set(o_["idx"][0].tolist())
+            topk_set_valid(gi, o_["s_doc"], w.k)
+            if set(gi[0].tolist()) == set(o_["idx"][0].tolist()):
+                assert_attention_close(host(g_["O"]), o_["O"])
