@@ -26,6 +26,15 @@
 namespace msa {
 namespace {
 
+// Split heuristics (compile-time knobs): splits target SPLIT_MUL workgroups
+// per CU in total, with at least MIN_TILES key tiles per split.
+#ifndef MSA_ATTEND_SPLIT_MUL
+#define MSA_ATTEND_SPLIT_MUL 4
+#endif
+#ifndef MSA_ATTEND_MIN_TILES
+#define MSA_ATTEND_MIN_TILES 2
+#endif
+
 constexpr int KT = 32;          // keys per tile
 constexpr int MAX_K = 256;      // selected documents per query
 constexpr float LOG2E = 1.4426950408889634f;
@@ -66,34 +75,6 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   const int g = a.h_q / a.h_kv;
   const int R = a.T * g;
 
-  // selected documents -> chunk prefix
-  if (threadIdx.x < 64) {
-    int carry = 0;
-    for (int base = 0; base < a.k; base += 64) {
-      const int r = base + lane;
-      int cnt = 0;
-      if (r < a.k) {
-        int doc = a.idx[(int64_t)q * a.k + r];
-        doc = doc < 0 ? 0 : (doc >= a.n_docs ? a.n_docs - 1 : doc);
-        const int64_t c0 = a.doc_chunk_off[doc];
-        cnt = (int)(a.doc_chunk_off[doc + 1] - c0);
-        sCB[r] = c0;
-      }
-      int x = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
-      if (r < a.k) sP[r] = carry + x - cnt;
-      carry += __shfl(x, 63, 64);
-    }
-    if (lane == 0) sP[a.k] = carry;
-  }
-  __syncthreads();
-  const int n_mem = sP[a.k];
-  const int n_keys = n_mem + a.L_loc;
-
   // this workgroup's rows and key range
   const int rb = rbg * WGW + wave;
   const int row = rb * 16 + col;               // this lane's query row (S^T / O^T column)
@@ -101,14 +82,8 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   const int t = row_ok ? row / g : 0;
   const int h = kvh * g + (row_ok ? row % g : 0);
   const int s_t = a.L_loc - a.T + t;           // local index of this row's token
-  const int last_row = std::min(R, (rbg * WGW + WGW) * 16) - 1;
-  const int s_last = a.L_loc - a.T + last_row / g;
-  int kps = (n_keys + n_split - 1) / n_split;
-  kps = (kps + KT - 1) / KT * KT;
-  const int k_lo = split * kps;
-  const int k_hi = std::min(std::min(n_keys, k_lo + kps), n_mem + s_last + 1);  // causal trim
-
-  // query fragments (B operand of S^T): dims [KW s + EL G, +EL), rotated at pos0 + s_t
+  // query fragments first: their loads overlap the document-prefix round trips
+  // (B operand of S^T): dims [KW s + EL G, +EL), rotated at pos0 + s_t
   FT qf[KS];
   {
     const T *qp = static_cast<const T *>(a.Q) + (((int64_t)q * a.T + t) * a.h_q + h) * D;
@@ -141,6 +116,41 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
     }
   }
 
+  // selected documents -> chunk prefix
+  if (threadIdx.x < 64) {
+    int carry = 0;
+    for (int base = 0; base < a.k; base += 64) {
+      const int r = base + lane;
+      int cnt = 0;
+      if (r < a.k) {
+        int doc = a.idx[(int64_t)q * a.k + r];
+        doc = doc < 0 ? 0 : (doc >= a.n_docs ? a.n_docs - 1 : doc);
+        const int64_t c0 = a.doc_chunk_off[doc];
+        cnt = (int)(a.doc_chunk_off[doc + 1] - c0);
+        sCB[r] = c0;
+      }
+      int x = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (r < a.k) sP[r] = carry + x - cnt;
+      carry += __shfl(x, 63, 64);
+    }
+    if (lane == 0) sP[a.k] = carry;
+  }
+  __syncthreads();
+  const int n_mem = sP[a.k];
+  const int n_keys = n_mem + a.L_loc;
+
+  const int last_row = std::min(R, (rbg * WGW + WGW) * 16) - 1;
+  const int s_last = a.L_loc - a.T + last_row / g;
+  int kps = (n_keys + n_split - 1) / n_split;
+  kps = (kps + KT - 1) / KT * KT;
+  const int k_lo = split * kps;
+  const int k_hi = std::min(std::min(n_keys, k_lo + kps), n_mem + s_last + 1);  // causal trim
+
   const float c2 = a.scale * LOG2E;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc_o[D / 16];
@@ -152,16 +162,25 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   const T *kloc = static_cast<const T *>(a.K_loc);
   const T *vloc = static_cast<const T *>(a.V_loc);
 
-  for (int kb = k_lo; kb < k_hi; kb += KT) {
-    // ---- gather the K / V^T tile -------------------------------------------
-    for (int u = threadIdx.x; u < KT * NP; u += NT) {
+  // ---- tile gather, split in two phases so that the next tile's global
+  // loads are in flight while the current tile is computed:
+  //   load:  unit u (key, segment pair m) of the tile -> raw 16-byte words in
+  //          registers, plus the RoPE position for local keys (-1: none)
+  //   store: rotate local keys, convert, write K and V^T into LDS
+  constexpr int UPT = (KT * NP + NT - 1) / NT;  // units per thread per tile (threads past the tile idle)
+  uint4 rk[UPT][2], rv[UPT][2];
+  int rpos[UPT];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = threadIdx.x + i * NT;
       const int key = u / NP, m = u % NP;
       const int j = kb + key;
-      float lo[EPS], hi[EPS], vlo[EPS], vhi[EPS];
       const T *ks = nullptr, *vs = nullptr;
-      bool rope = false;
-      int pos = 0;
-      if (j < k_hi && j < n_mem) {
+      rpos[i] = -1;
+      if (u >= KT * NP) {
+        // no unit for this thread
+      } else if (j < k_hi && j < n_mem) {
         int lo_r = 0, hi_r = a.k - 1;  // rank r with sP[r] <= j < sP[r+1]
         while (lo_r < hi_r) {
           const int mid = (lo_r + hi_r + 1) >> 1;
@@ -176,42 +195,50 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
         const int64_t off = (((int64_t)q * a.L_loc + s) * a.h_kv + kvh) * D;
         ks = kloc + off;
         vs = vloc + off;
-        rope = true;
-        pos = a.pos0 + s;
+        rpos[i] = a.pos0 + s;
       }
       if (ks) {
-        const T *pk[2] = {ks + m * EPS, ks + D / 2 + m * EPS};
-        const T *pv[2] = {vs + m * EPS, vs + D / 2 + m * EPS};
-        float *dk[2] = {lo, hi}, *dv[2] = {vlo, vhi};
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const uint4 rk = *reinterpret_cast<const uint4 *>(pk[p]);
-          const uint4 rv = *reinterpret_cast<const uint4 *>(pv[p]);
-          const uint32_t wk[4] = {rk.x, rk.y, rk.z, rk.w}, wv[4] = {rv.x, rv.y, rv.z, rv.w};
-          if constexpr (EPS == 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { dk[p][e] = __uint_as_float(wk[e]); dv[p][e] = __uint_as_float(wv[e]); }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              dk[p][2 * e] = __uint_as_float(wk[e] << 16); dk[p][2 * e + 1] = __uint_as_float(wk[e] & 0xFFFF0000u);
-              dv[p][2 * e] = __uint_as_float(wv[e] << 16); dv[p][2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u);
-            }
-          }
-        }
-        if (rope) {
-          const int64_t crow = (int64_t)pos * (D / 2) + m * EPS;
-#pragma unroll
-          for (int e = 0; e < EPS; ++e) {
-            const float c = a.cos[crow + e], sn = a.sin[crow + e];
-            const float x0 = lo[e], x1 = hi[e];
-            lo[e] = x0 * c - x1 * sn;
-            hi[e] = x0 * sn + x1 * c;
-          }
-        }
+        rk[i][0] = *reinterpret_cast<const uint4 *>(ks + m * EPS);
+        rk[i][1] = *reinterpret_cast<const uint4 *>(ks + D / 2 + m * EPS);
+        rv[i][0] = *reinterpret_cast<const uint4 *>(vs + m * EPS);
+        rv[i][1] = *reinterpret_cast<const uint4 *>(vs + D / 2 + m * EPS);
       } else {
+        rk[i][0] = rk[i][1] = rv[i][0] = rv[i][1] = uint4{0u, 0u, 0u, 0u};  // zeros: no NaN reaches P*V
+      }
+    }
+  };
+  auto store_tile = [&]() {
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) lo[e] = hi[e] = vlo[e] = vhi[e] = 0.f;
+    for (int i = 0; i < UPT; ++i) {
+      const int u = threadIdx.x + i * NT;
+      if (u >= KT * NP) continue;
+      const int key = u / NP, m = u % NP;
+      float lo[EPS], hi[EPS], vlo[EPS], vhi[EPS];
+      float *dk[2] = {lo, hi}, *dv[2] = {vlo, vhi};
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t wk[4] = {rk[i][p].x, rk[i][p].y, rk[i][p].z, rk[i][p].w};
+        const uint32_t wv[4] = {rv[i][p].x, rv[i][p].y, rv[i][p].z, rv[i][p].w};
+        if constexpr (EPS == 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { dk[p][e] = __uint_as_float(wk[e]); dv[p][e] = __uint_as_float(wv[e]); }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dk[p][2 * e] = __uint_as_float(wk[e] << 16); dk[p][2 * e + 1] = __uint_as_float(wk[e] & 0xFFFF0000u);
+            dv[p][2 * e] = __uint_as_float(wv[e] << 16); dv[p][2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u);
+          }
+        }
+      }
+      if (rpos[i] >= 0) {
+        const int64_t crow = (int64_t)rpos[i] * (D / 2) + m * EPS;
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const float c = a.cos[crow + e], sn = a.sin[crow + e];
+          const float x0 = lo[e], x1 = hi[e];
+          lo[e] = x0 * c - x1 * sn;
+          hi[e] = x0 * sn + x1 * c;
+        }
       }
       T *dK = sK + key * KROW + m * EPS;
 #pragma unroll
@@ -222,6 +249,12 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
         sV[(D / 2 + m * EPS + e) * VROW + key] = Elem<T>::from_f32(vhi[e]);
       }
     }
+  };
+
+  if (k_lo < k_hi) load_tile(k_lo);
+  for (int kb = k_lo; kb < k_hi; kb += KT) {
+    store_tile();
+    if (kb + KT < k_hi) load_tile(kb + KT);  // next tile in flight during this one
     __syncthreads();
 
     if (rb * 16 < R) {
@@ -361,8 +394,8 @@ Plan plan(const AttendArgs &a) {
   const int64_t base = (int64_t)a.n_q * a.h_kv * p.n_rbg;
   const int64_t est_keys = std::min<int64_t>((int64_t)a.k * std::max(1, a.max_doc_chunks), a.n_chunks) + a.L_loc;
   const int64_t tiles = (est_keys + KT - 1) / KT;
-  int64_t ns = (4LL * device_cu_count() + base - 1) / base;
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / 2));
+  int64_t ns = ((int64_t)MSA_ATTEND_SPLIT_MUL * device_cu_count() + base - 1) / base;
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / MSA_ATTEND_MIN_TILES));
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, 64));
   p.n_split = (int)ns;
   return p;

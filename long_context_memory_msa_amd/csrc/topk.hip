@@ -11,6 +11,10 @@
 //           stopping as soon as the boundary digit bin is taken whole);
 //   pass 2: one workgroup per query selects the top-k of the candidates
 //           the same way and sorts them (bitonic, in LDS).
+// Up to 8K documents per query a single pass does it all: one 1024-thread
+// workgroup per query holds the whole row in registers (24 composites per
+// thread), radix-selects with per-wave LDS histograms, compacts the k winners
+// and sorts them.
 #include <algorithm>
 
 #include "msa_device.hpp"
@@ -30,6 +34,25 @@ struct SelShared {
   uint32_t above;    // elements with a larger digit among the matching ones
   uint32_t in_bin;   // elements in the chosen bin
 };
+
+// Single-pass limit (documents per query), a compile-time knob.
+#ifndef MSA_TOPK_SINGLE_MAX
+#define MSA_TOPK_SINGLE_MAX 8192
+#endif
+
+// Histogram add for a digit that most lanes share (the first, sign/exponent
+// digit of cosine scores): one LDS atomic per distinct digit in the wave
+// instead of one per lane.  Every lane of the wave must call it.
+__device__ __forceinline__ void hist_add_wave(uint32_t *hist, uint32_t digit, bool active) {
+  unsigned long long pending = __ballot(active);
+  while (pending) {
+    const int leader = __ffsll((long long)pending) - 1;
+    const uint32_t d = __shfl(digit, leader, 64);
+    const unsigned long long same = __ballot(active && digit == d);
+    if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[d], (uint32_t)__popcll(same));
+    pending &= ~same;
+  }
+}
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int64_t i) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
@@ -67,10 +90,13 @@ __device__ void radix_select(Get get, int64_t n, uint32_t need, SelShared &sh, i
   for (;; shift -= 8) {
     for (int b = threadIdx.x; b < 256; b += TK_THREADS) sh.hist[b] = 0;
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < n; i += TK_THREADS) {
-      const uint64_t v = get(i);
-      const bool match = (shift == 56) || ((v ^ prefix) >> (shift + 8)) == 0;
-      if (match) atomicAdd(&sh.hist[(v >> shift) & 255], 1u);
+    for (int64_t base = 0; base < n; base += TK_THREADS) {
+      const int64_t i = base + threadIdx.x;
+      const uint64_t v = i < n ? get(i) : 0;
+      const bool match = i < n && ((shift == 56) || ((v ^ prefix) >> (shift + 8)) == 0);
+      const uint32_t digit = (uint32_t)(v >> shift) & 255;
+      if (shift == 56) hist_add_wave(sh.hist, digit, match);
+      else if (match) atomicAdd(&sh.hist[digit], 1u);
     }
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -200,16 +226,155 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass2(const uint64_t *cand, i
   }
 }
 
+// ---- single pass: one 1024-thread workgroup per query ---------------------
+constexpr int TS_THREADS = 1024;
+constexpr int TS_ITEMS = 24;
+constexpr int TS_WAVES = TS_THREADS / 64;
+
+struct SingleShared {
+  uint32_t hist[TS_WAVES][256];   // per-wave histograms
+  uint32_t total[256];
+  int32_t wave_tot[TS_WAVES];
+  uint32_t bin, above, in_bin;
+  uint64_t sel[TK_MAX_K];
+};
+
+template <bool FROM_KEYS>
+__global__ __launch_bounds__(TS_THREADS) void topk_single(const float *scores, const uint32_t *keys, int n_docs,
+                                                             int k, int kpad, int32_t *idx, float *val) {
+  __shared__ SingleShared sh;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = (int64_t)q * n_docs;
+  uint64_t v[TS_ITEMS];
+#pragma unroll
+  for (int j = 0; j < TS_ITEMS; ++j) {
+    const int i = j * TS_THREADS + tid;  // coalesced
+    uint64_t x = 0;
+    if (i < n_docs) x = composite(FROM_KEYS ? keys[row + i] : score_key(scores[row + i]), i);
+    v[j] = x;
+  }
+  // radix select, MSB first, 8 bits per pass, stopping when the boundary bin is taken whole
+  uint64_t prefix = 0;
+  uint32_t need = (uint32_t)k;
+  int shift = 56;
+  for (;; shift -= 8) {
+    for (int e = tid; e < TS_WAVES * 256; e += TS_THREADS) (&sh.hist[0][0])[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TS_ITEMS; ++j) {
+      const bool match = v[j] != 0 && ((shift == 56) || ((v[j] ^ prefix) >> (shift + 8)) == 0);
+      const uint32_t digit = (uint32_t)(v[j] >> shift) & 255;
+      if (shift == 56) hist_add_wave(sh.hist[wave], digit, match);
+      else if (match) atomicAdd(&sh.hist[wave][digit], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < TS_WAVES; ++w) t += sh.hist[w][tid];
+      sh.total[tid] = t;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t c[4], s = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = sh.total[255 - 4 * lane - j];
+        s += c[j];
+      }
+      uint32_t incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const unsigned long long m = __ballot(incl >= need);
+      const int first = __ffsll((long long)m) - 1;
+      if (lane == first) {
+        uint32_t cum = incl - s;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= need) {
+            sh.bin = 255 - 4 * lane - j;
+            sh.above = cum;
+            sh.in_bin = c[j];
+            break;
+          }
+          cum += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sh.bin, above = sh.above, in_bin = sh.in_bin;
+    prefix |= (uint64_t)bin << shift;
+    need -= above;
+    if (in_bin == need || shift == 0) break;
+  }
+  // compact the k winners into LDS (positions from a block prefix sum), then sort
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < TS_ITEMS; ++j) cnt += (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift));
+  int x = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh.wave_tot[wave] = x;
+  for (int e = tid; e < kpad; e += TS_THREADS) sh.sel[e] = 0;
+  __syncthreads();
+  int pos = x - cnt;
+  for (int w = 0; w < wave; ++w) pos += sh.wave_tot[w];
+#pragma unroll
+  for (int j = 0; j < TS_ITEMS; ++j)
+    if (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift)) sh.sel[pos++] = v[j];
+  __syncthreads();
+  for (int size = 2; size <= kpad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (tid < kpad) {
+        const int j = tid ^ stride;
+        if (j > tid) {
+          const uint64_t a = sh.sel[tid], b = sh.sel[j];
+          const bool desc = (tid & size) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            sh.sel[tid] = b;
+            sh.sel[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < k) {
+    const uint64_t w64 = sh.sel[tid];
+    idx[(int64_t)q * k + tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)w64);
+    val[(int64_t)q * k + tid] = key_score((uint32_t)(w64 >> 32));
+  }
+}
+
 int n_slices_for(int n_docs) { return (n_docs + TK_SLICE - 1) / TK_SLICE; }
 
 }  // namespace
 
+bool topk_single_pass(int n_docs) { return n_docs <= TS_THREADS * TS_ITEMS && n_docs <= MSA_TOPK_SINGLE_MAX; }
+
 size_t topk_ws_bytes(int n_q, int n_docs, int k) {
+  if (topk_single_pass(n_docs)) return 0;
   return (size_t)n_q * n_slices_for(n_docs) * k * sizeof(uint64_t);
 }
 
 hipError_t launch_topk(const float *scores, const uint32_t *keys, int n_q, int n_docs, int k, int32_t *idx, float *val,
                        void *ws, hipStream_t s) {
+  int kpad = 1;
+  while (kpad < k) kpad <<= 1;
+  if (topk_single_pass(n_docs)) {
+    if (keys)
+      hipLaunchKernelGGL(topk_single<true>, dim3(n_q), dim3(TS_THREADS), 0, s, scores, keys, n_docs, k, kpad, idx, val);
+    else
+      hipLaunchKernelGGL(topk_single<false>, dim3(n_q), dim3(TS_THREADS), 0, s, scores, keys, n_docs, k, kpad, idx,
+                         val);
+    return hipGetLastError();
+  }
   const int ns = n_slices_for(n_docs);
   uint64_t *cand = static_cast<uint64_t *>(ws);
   dim3 g1(ns, n_q);
@@ -219,8 +384,6 @@ hipError_t launch_topk(const float *scores, const uint32_t *keys, int n_q, int n
     hipLaunchKernelGGL(topk_pass1<false>, g1, dim3(TK_THREADS), 0, s, scores, keys, n_docs, k, ns, cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int kpad = 1;
-  while (kpad < k) kpad <<= 1;
   hipLaunchKernelGGL(topk_pass2, dim3(n_q), dim3(TK_THREADS), 0, s, cand, (int64_t)ns * k, k, kpad, idx, val);
   return hipGetLastError();
 }

@@ -142,7 +142,9 @@ def test_route_isolated(device, name, t_r, n_q):
 
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n_q,n_docs,k", [(1, 7, 1), (1, 7, 7), (3, 2048, 16), (2, 5000, 256), (16, 23048, 16),
-                                          (4, 4099, 64), (1, 300, 256)])
+                                          (4, 4099, 64), (1, 300, 256), (1, 24576, 256),
+                                          # above 24K documents per query: the two-pass path
+                                          (2, 24577, 16), (3, 60000, 64), (1, 100000, 256)])
 def test_topk_isolated(device, n_q, n_docs, k):
     log(f"topk n_q={n_q} n_docs={n_docs} k={k}")
     s = W.scores_for_topk(1000 + n_docs + k, n_q, n_docs)
