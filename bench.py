@@ -117,6 +117,90 @@ def cpu_baseline(w, qi, n_docs: int) -> dict:
     }
 
 
+def bench_interleave(args) -> int:
+    """18 routed layers x 10M-token banks, 3 rounds of route -> top-k -> attend
+    (prefill 512 tokens, then 64 appended per round): throughput and the MFMA
+    rooflines of the router scan and of attention."""
+    import numpy as np
+    import torch
+
+    from synth import device as sdev, workloads as W
+    from long_context_memory_msa_amd import _lib as L, memory as M, offline
+
+    dev = torch.device("cuda:0")
+    w = W.make_workload(4)
+    print(f"[bench] {w.name}: {w.n_layers} layers x {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks",
+          file=sys.stderr, flush=True)
+    banks, layers = [], []
+    rope = None
+    for layer in range(w.n_layers):
+        bank = M.Bank(w.doc_lens, w.chunk, w.h_kv, w.d, w.h_r, w.d_r, w.dtype, dev)
+        rope = rope or M.Rope(w.max_pos, w.d, w.rope_base, dev)
+        offline.encode_bank(bank, rope, lambda a, b, K, V, KR, l=layer: sdev.fill_raw_slab(w, l, a, b, K, V, KR),
+                            args.slab_tokens, w.h_kv, w.d, w.h_r, w.d_r)
+        banks.append(bank)
+        qi = W.query_inputs(w, layer)
+        layers.append({k: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev).to(torch.bfloat16)
+                       for k, v in qi.items()})
+    calls = [(r, l) for r in range(w.rounds) for l in range(w.n_layers)]
+    shapes = {}
+    for r in range(w.rounds):
+        L_act = w.L_loc + w.append * r
+        shapes[r] = (L_act, w.L_loc if r == 0 else w.append)
+    nb = max(L.msa_layer_workspace_bytes(banks[0].c, 1, T, La, La, w.h_q, w.k) for La, T in shapes.values())
+    ws = M.workspace(nb, dev)
+    outs = {r: torch.empty((1, shapes[r][1], w.h_q, w.d), dtype=torch.bfloat16, device=dev) for r in shapes}
+    idxs = {c: torch.empty((1, w.k), dtype=torch.int32, device=dev) for c in calls}
+    val = torch.empty((1, w.k), dtype=torch.float32, device=dev)
+    scale = L.default_scale(w.d)
+
+    def run(events=None):
+        for i, (r, l) in enumerate(calls):
+            La, T = shapes[r]
+            inp = layers[l]
+            L.msa_layer_forward(banks[l].c, inp["Q"][:, La - T:La], inp["K_loc"][:, :La], inp["V_loc"][:, :La],
+                                inp["QR"][:, :La], 1, T, La, La, w.h_q, w.k, w.pos0, scale, rope.c, outs[r],
+                                idxs[(r, l)], val, None, ws, nb, None if events is None else events[4 * i:4 * i + 4])
+
+    run()
+    torch.cuda.synchronize()
+    ev = Events(4 * len(calls))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(ev.h)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    route = [ev.ms(ev.h[4 * i], ev.h[4 * i + 1]) for i in range(len(calls))]
+    attend = [ev.ms(ev.h[4 * i + 2], ev.h[4 * i + 3]) for i in range(len(calls))]
+    off = w.doc_chunk_off
+    route_flop = attn_flop = 0.0
+    for (r, l) in calls:
+        La, T = shapes[r]
+        route_flop += 2.0 * La * w.n_chunks * w.h_r * w.d_r
+        sel = idxs[(r, l)].cpu().numpy()[0]
+        n_mem = int(sum(off[d + 1] - off[d] for d in sel))
+        visible = sum(n_mem + (La - T + t) + 1 for t in range(T))
+        attn_flop += 4.0 * w.h_q * w.d * visible
+    peak = 2.5e15
+    rec = {
+        "metric": "Memory Interleave: memory tokens routed/sec over 18 layers x 3 rounds (10M-token banks)",
+        "value": w.n_tok * len(calls) / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "ms_per_interleave": wall * 1e3,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "18 routed layers x 10M tokens, docs U[256,4096], chunk 128, prefill 512 + 2 x 64, k=8",
+                   "n_chunks_per_layer": w.n_chunks, "layer_calls": len(calls)},
+        "route": {"ms_total": sum(route), "tflop": route_flop / 1e12,
+                  "mfma_frac": route_flop / (sum(route) * 1e-3) / peak, "peak_tflops": peak / 1e12},
+        "attend": {"ms_total": sum(attend), "tflop": attn_flop / 1e12,
+                   "mfma_frac": attn_flop / (sum(attend) * 1e-3) / peak, "peak_tflops": peak / 1e12},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +210,9 @@ def main() -> int:
                     help="oracle baseline sample: first N documents (-1 = the whole bank, 0 = skip)")
     ap.add_argument("--bank-tokens", type=int, default=None, help="smaller bank for a quick look (not the metric)")
     ap.add_argument("--slab-tokens", type=int, default=8_000_000)
+    ap.add_argument("--workload", choices=["decode100m", "interleave"], default="decode100m",
+                    help="decode100m: the headline layer (default); interleave: 18 routed layers x 10M tokens, "
+                         "3 Memory Interleave rounds (MFMA-bound prefill report)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -153,6 +240,8 @@ def main() -> int:
     from long_context_memory_msa_amd import _lib as L, memory as M, offline
 
     dev = torch.device("cuda:0")
+    if args.workload == "interleave":
+        return bench_interleave(args)
     w = W.make_workload(3, bank_tokens=args.bank_tokens)
     print(f"[bench] {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr, flush=True)
 

@@ -150,6 +150,7 @@ msa::RouteArgs route_args(const msa_bank *b, const void *qr, int32_t n_q, int32_
   a.t_r = t_r;
   a.doc_keys = doc_keys;
   a.chunk_out = chunk_out;
+  a.qinv = nullptr;
   return a;
 }
 
@@ -167,7 +168,7 @@ struct LayerWs {
 LayerWs layer_ws(const msa_bank *b, int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k) {
   LayerWs w;
   w.scores = align_up((size_t)n_q * b->n_docs * sizeof(uint32_t));
-  w.route = align_up(msa::route_ws_bytes(b->n_chunks, n_q, t_r));
+  w.route = align_up(msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, n_q, t_r));
   w.topk = align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
   msa::AttendArgs a = attend_args(b, nullptr, nullptr, nullptr, n_q, T, L_loc, h_q, nullptr, k, 0, 1.f, nullptr, nullptr);
   w.attend = align_up(msa::attend_ws_bytes(a));
@@ -296,7 +297,7 @@ int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void 
 
 size_t msa_route_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t t_r) {
   if (!b || n_q < 1 || t_r < 1 || b->n_chunks < 1) return 0;
-  return msa::route_ws_bytes(b->n_chunks, n_q, t_r);
+  return msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, n_q, t_r);
 }
 
 int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *s_doc, float *s_chunk,
@@ -308,7 +309,7 @@ int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r,
     if (rc) return rc;
     CHECK_PTR(s_doc, 4, "s_doc");
     if (s_chunk && !aligned(s_chunk, 4)) return fail(MSA_ERR_ARG, "s_chunk is not 4-byte aligned");
-    const size_t need = msa::route_ws_bytes(b->n_chunks, n_q, t_r);
+    const size_t need = msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, n_q, t_r);
     if (need && (!ws || ws_bytes < need || !aligned(ws, 16)))
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
     hipStream_t s = (hipStream_t)stream;
@@ -323,7 +324,9 @@ int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r,
       uint32_t *dk = reinterpret_cast<uint32_t *>(s_doc);
       e = msa::launch_fill_u32(dk, nd, 0u, s);
       if (e == hipSuccess && ck) e = msa::launch_fill_u32(ck, nc, 0u, s);
-      if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, qr, n_q, t_r, nullptr, nullptr, dk, ck), s);
+      msa::RouteArgs a = route_args(b, qr, n_q, t_r, nullptr, nullptr, dk, ck);
+      a.qinv = static_cast<float *>(ws);
+      if (e == hipSuccess) e = msa::launch_route_scan(a, s);
       if (e == hipSuccess) e = msa::launch_keys_to_scores(dk, nd, s);
       if (e == hipSuccess && ck) e = msa::launch_keys_to_scores(ck, nc, s);
     }
@@ -438,7 +441,9 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
       uint32_t *keys = reinterpret_cast<uint32_t *>(w);
       e = msa::launch_fill_u32(keys, nd, 0u, s);
       if (e == hipSuccess) e = rec(0);
-      if (e == hipSuccess) e = msa::launch_route_scan(route_args(b, QR, n_q, t_r, nullptr, nullptr, keys, nullptr), s);
+      msa::RouteArgs ra = route_args(b, QR, n_q, t_r, nullptr, nullptr, keys, nullptr);
+      ra.qinv = static_cast<float *>(rt_ws);
+      if (e == hipSuccess) e = msa::launch_route_scan(ra, s);
       if (e == hipSuccess) e = rec(1);
       if (e == hipSuccess) e = msa::launch_topk(nullptr, keys, n_q, b->n_docs, k, idx, val, tk_ws, s);
       if (e == hipSuccess) e = rec(2);

@@ -48,9 +48,14 @@ struct RouteArgs {
   uint32_t *doc_keys;            // [n_q][n_docs]
   // optional per-chunk scores [n_q][n_chunks]: fp32 in single-writer mode, keys otherwise
   uint32_t *chunk_out;
+  // many-row (wide) scan: (1/h_r)/||Q^R|| per query row and head, [n_q * t_r][h_r] (workspace)
+  float *qinv;
 };
 bool route_single_writer(int t_r);                    // (query, document) scores have one writer
-size_t route_ws_bytes(int64_t n_chunks, int n_q, int t_r);
+bool route_use_wide(int dtype, int h_r, int d_r, int t_r);     // GEMM-tiled scan for many rows per query
+size_t route_wide_ws_bytes(int n_q, int t_r, int h_r);
+size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_q, int t_r);
+hipError_t launch_route_wide(const RouteArgs &a, hipStream_t s);
 hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);

@@ -386,10 +386,13 @@ hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s) {
 
 bool route_single_writer(int t_r) { return t_r == 1 || t_r == 16; }
 
-size_t route_ws_bytes(int64_t n_chunks, int n_q, int t_r) {
-  if (!route_single_writer(t_r)) return 0;
-  const int64_t rbs = ((int64_t)n_q * t_r + 15) / 16;
-  return (size_t)rbs * ((n_chunks + 15) / 16) * 32 * sizeof(float);
+size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_q, int t_r) {
+  if (route_single_writer(t_r)) {
+    const int64_t rbs = ((int64_t)n_q * t_r + 15) / 16;
+    return (size_t)rbs * ((n_chunks + 15) / 16) * 32 * sizeof(float);
+  }
+  if (route_use_wide(dtype, h_r, d_r, t_r)) return route_wide_ws_bytes(n_q, t_r, h_r);
+  return 0;
 }
 
 hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s) {
@@ -401,6 +404,7 @@ hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s) {
 
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s) {
   if (a.n_chunks == 0) return hipSuccess;
+  if (!a.edges && a.qinv && route_use_wide(a.dtype, a.h_r, a.d_r, a.t_r)) return launch_route_wide(a, s);
   if (a.dtype == 0) return a.d_r == 64 ? route_by_hr<float, 64>(a, s) : route_by_hr<float, 128>(a, s);
   return a.d_r == 64 ? route_by_hr<bf16_t, 64>(a, s) : route_by_hr<bf16_t, 128>(a, s);
 }

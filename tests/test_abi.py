@@ -108,13 +108,14 @@ def test_route_validation():
 
 
 def test_topk_validation_and_workspace():
-    assert msa.msa_topk_workspace_bytes(2, 5000, 16) == 2 * 3 * 16 * 8
+    assert msa.msa_topk_workspace_bytes(2, 5000, 16) == 0                 # one pass per query
+    assert msa.msa_topk_workspace_bytes(2, 20000, 16) == 2 * 10 * 16 * 8  # 2048-document slices
     assert msa.msa_topk_workspace_bytes(1, 10, 11) == 0
     assert _code(msa.msa_topk, A, 1, 10, 11, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG      # k > n_docs
     assert _code(msa.msa_topk, A, 1, 1000, 257, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG   # k > 256
     assert _code(msa.msa_topk, A, 1, 1000, 0, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG
-    assert _code(msa.msa_topk, A, 1, 5000, 16, A, A, A, 100, 0) == L.MSA_ERR_WORKSPACE
-    assert _code(msa.msa_topk, A, 1, 5000, 16, A, A, None, 1 << 20, 0) == L.MSA_ERR_WORKSPACE
+    assert _code(msa.msa_topk, A, 1, 20000, 16, A, A, A, 100, 0) == L.MSA_ERR_WORKSPACE
+    assert _code(msa.msa_topk, A, 1, 20000, 16, A, A, None, 1 << 20, 0) == L.MSA_ERR_WORKSPACE
 
 
 def test_attend_validation():

@@ -111,7 +111,8 @@ def test_pool_edge_lengths(device, dtype):
 
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name,t_r,n_q", [("cfg0", 16, 1), ("cfg1", 128, 1), ("cfg1", 1, 1), ("cfg1", 5, 3),
-                                          ("cfg1", 40, 2), ("cfg1", 16, 3), ("cfg1", 1, 37), ("cfg2", 256, 1),
+                                          ("cfg1", 40, 2), ("cfg1", 16, 3), ("cfg1", 1, 37), ("cfg1", 48, 3),
+                                          ("cfg1", 64, 5), ("cfg2", 256, 1),
                                           ("cfg3", 1, 16)])
 def test_route_isolated(device, name, t_r, n_q):
     cfg, bt = SMALL[name]
