@@ -35,13 +35,15 @@ namespace msa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int MW = 128;  // rows per workgroup
 constexpr int NW = 128;  // chunks per workgroup
 
-// qinv[row][h] = (1/H_r) / ||Q^R[row][h]|| (0 for a zero row); 16 lanes per (row, head)
+// qinv[h][row] = (1/H_r) / ||Q^R[row][h]|| (0 for a zero row); 16 lanes per (row, head)
 template <int DR>
-__global__ void q_inv_norm_kernel(const bf16_t *qr, int n_pairs, int h_r, float *qinv) {
+__global__ void q_inv_norm_kernel(const bf16_t *qr, int n_rows, int h_r, float *qinv) {
+  const int n_pairs = n_rows * h_r;
   constexpr int SEGS = DR / 8;  // 16-byte segments per row slice
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t pair = t / SEGS;
@@ -58,22 +60,43 @@ __global__ void q_inv_norm_kernel(const bf16_t *qr, int n_pairs, int h_r, float 
   }
 #pragma unroll
   for (int o = SEGS / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if (pair < n_pairs && seg == 0) qinv[pair] = ss > 0.f ? (1.0f / sqrtf(ss)) * (1.0f / h_r) : 0.f;
+  if (pair < n_pairs && seg == 0)
+    qinv[(pair % h_r) * n_rows + pair / h_r] = ss > 0.f ? (1.0f / sqrtf(ss)) * (1.0f / h_r) : 0.f;
+}
+
+// XOR swizzle of the eight 16-byte slots of a 128-byte chunk row in LDS: rows
+// r..r+7 (and the even / odd rows of r..r+15) put a given logical slot in
+// eight different bank groups, so fragment reads of 16 rows are conflict-free.
+__device__ __forceinline__ int slot_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most N vector-memory
+// operations of this wave are outstanding, leaving the other counters alone
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) only
+
+// Workgroup barrier for the stage pipeline, without the memory fence of
+// __syncthreads (whose full vmcnt(0) wait would also wait for the fills in
+// flight): this wave's LDS reads have returned (lgkmcnt 0) and its fills of
+// the next stage have landed (explicit vmcnt wait before the call).
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(LGKM0);
+  __builtin_amdgcn_s_barrier();
 }
 
 template <int HR, int DR>
-__global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_mtiles,
-                                                                 int64_t n_ntiles) {
-  constexpr int SD = DR / 2;             // one stage = half of a head's dimensions
-  constexpr int PITCH = SD + 8;          // LDS row pitch (elements): conflict-free fragment reads
-  constexpr int KS = SD / 32;            // MFMA k-steps per stage
-  constexpr int SEGS = SD / 8;           // 16-byte segments per row per stage
-  constexpr int SPT = MW * SEGS / 256;   // segments per thread per operand
-  __shared__ __align__(16) bf16_t sA[MW * PITCH];
-  __shared__ __align__(16) bf16_t sB[NW * PITCH];
-  __shared__ float red[MW / 16][NW];     // per row block: max over its 16 rows
+__global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_mtiles, int64_t n_ntiles) {
+  static_assert(DR == 128, "stage layout assumes 128-dim router heads");
+  constexpr int SD = DR / 2;       // one stage = half of a head's dimensions (128 bytes per row)
+  constexpr int FILLS = 4;         // direct-to-LDS loads per wave per operand per stage
+  // Stage buffers (rows of 128 bytes, slots swizzled, filled by direct-to-LDS
+  // loads), double-buffered: buffers 0 hold the first half of a head, buffers
+  // 1 the second.  Each buffer is its own variable so that the compiler can
+  // tell the buffer being filled from the one being read and does not wait
+  // for the fill in flight.
+  __shared__ __align__(16) bf16_t sA0[MW * SD], sA1[MW * SD];  // query rows
+  __shared__ __align__(16) bf16_t sB0[NW * SD], sB1[NW * SD];  // chunk rows
   __shared__ __align__(16) float sqi[HR][MW];  // (1/H_r)/||Q^R|| of the tile's rows
-  __shared__ int sdoc[NW];
+  __shared__ float sik[HR][NW];                // 1/||Kbar^R|| of the tile's chunks
 
   // tile order: row tiles of one chunk tile share blockIdx % 8 (one XCD)
   const int b = blockIdx.x;
@@ -87,58 +110,43 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
   const int wr = wave >> 1, wc = wave & 1;  // 2 x 2 waves of 64 rows x 64 chunks
   const int n_rows = a.n_q * a.t_r;
   const int64_t row0 = (int64_t)m_tile * MW, c0 = n_tile * NW;
-  const bf16_t *qr = static_cast<const bf16_t *>(a.qr);
-  const bf16_t *kr = static_cast<const bf16_t *>(a.krbar);
+  const int rows_here = (int)std::min<int64_t>(MW, n_rows - row0);
+  const int chunks_here = (int)std::min<int64_t>(NW, a.n_chunks - c0);
+  const bf16_t *qt = static_cast<const bf16_t *>(a.qr) + row0 * HR * DR;    // this tile's rows
+  const bf16_t *kt = static_cast<const bf16_t *>(a.krbar) + c0 * HR * DR;   // this tile's chunks
   const int rot = (int)(n_tile % HR);
 
-  // staging of one stage's slices: global -> registers (issued a stage ahead) -> LDS
-  u32x4 ra[SPT], rb[SPT];
-  float ikn[4];  // 1/||Kbar^R|| of this lane's four chunk columns for the next head
-  // rows and chunks past the end read the last valid one (clamped, no branch):
-  // their results are discarded by the epilogue (row blocks past n_rows, chunks
-  // without a document).  Per stage a thread moves SPT 16-byte segments of each
-  // operand: rows tid / SEGS + i * (256 / SEGS), segment tid % SEGS.
-  const int seg = tid % SEGS;
-  const bf16_t *pa[SPT];
-  const bf16_t *pb[SPT];
+  // Fill of a stage: wave w writes rows 32w .. 32w+31 with four loads; in load
+  // p, lane L writes row 32w + 8p + L/8 at physical slot L%8, which holds the
+  // logical slot (L%8) ^ slot_swz(row).  Rows and chunks past the end read the
+  // last valid one (clamped, no branch); the epilogue discards them.
+  uint32_t aoff[FILLS], boff[FILLS];
 #pragma unroll
-  for (int i = 0; i < SPT; ++i) {
-    const int row = tid / SEGS + i * (256 / SEGS);
-    const int64_t m = std::min<int64_t>(row0 + row, n_rows - 1), c = std::min<int64_t>(c0 + row, a.n_chunks - 1);
-    pa[i] = qr + m * HR * DR + seg * 8;
-    pb[i] = kr + c * HR * DR + seg * 8;
+  for (int p = 0; p < FILLS; ++p) {
+    const int row = 32 * wave + 8 * p + lane / 8;
+    const int slot = (lane % 8) ^ slot_swz(row);
+    aoff[p] = (uint32_t)(std::min(row, rows_here - 1) * HR * DR + slot * 8);
+    boff[p] = (uint32_t)(std::min(row, chunks_here - 1) * HR * DR + slot * 8);
   }
-  const float *pik[4];
+  auto fill = [&](bf16_t *dA, bf16_t *dB, int h, int half) {
+    const int o = h * DR + half * SD;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pik[j] = a.kr_inv_norm + std::min<int64_t>(c0 + 64 * wc + 16 * j + col, a.n_chunks - 1) * HR;
-  auto load = [&](int h, int half) {
-    const int off = h * DR + half * SD;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4 *>(pa[i] + off);
-      rb[i] = *reinterpret_cast<const u32x4 *>(pb[i] + off);
-    }
-    if (half == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ikn[j] = pik[j][h];
+    for (int p = 0; p < FILLS; ++p) {
+      __builtin_amdgcn_global_load_lds(qt + aoff[p] + o, (lds_void *)(dA + (32 * wave + 8 * p) * SD), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kt + boff[p] + o, (lds_void *)(dB + (32 * wave + 8 * p) * SD), 16, 0, 0);
     }
   };
-  auto store = [&]() {
+  // k-step ks of a stage pairs logical slot 2G + ks of a query row and of a
+  // chunk row: lane group G covers the stage's dimensions 16G .. 16G+15
+  auto multiply = [&](const bf16_t *sA, const bf16_t *sB, f32x4 (&acc)[4][4]) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int row = tid / SEGS + i * (256 / SEGS);
-      *reinterpret_cast<u32x4 *>(sA + row * PITCH + seg * 8) = ra[i];
-      *reinterpret_cast<u32x4 *>(sB + row * PITCH + seg * 8) = rb[i];
-    }
-  };
-  auto multiply = [&](f32x4 (&acc)[4][4]) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       bf16x8 fa[4], fb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        fa[i] = load_frag<bf16_t>(sA + (64 * wr + 16 * i + col) * PITCH + ks * 32 + G * 8);
-        fb[i] = load_frag<bf16_t>(sB + (64 * wc + 16 * i + col) * PITCH + ks * 32 + G * 8);
+        const int ra = 64 * wr + 16 * i + col, rb = 64 * wc + 16 * i + col;
+        fa[i] = *reinterpret_cast<const bf16x8 *>(sA + ra * SD + ((2 * G + ks) ^ slot_swz(ra)) * 8);
+        fb[i] = *reinterpret_cast<const bf16x8 *>(sB + rb * SD + ((2 * G + ks) ^ slot_swz(rb)) * 8);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -153,33 +161,39 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
 #pragma unroll
     for (int j = 0; j < 4; ++j) score[i][j] = zero4();
 
-  if (tid < NW) sdoc[tid] = (c0 + tid < a.n_chunks) ? a.chunk_doc[c0 + tid] : -1;
+  // scales of the tile's rows and chunks (qinv is [h][n_rows], kr_inv_norm [chunk][h])
   for (int k = tid; k < MW * HR; k += 256) {
-    const int row = k / HR, h = k % HR;
-    sqi[h][row] = row0 + row < n_rows ? a.qinv[(row0 + row) * HR + h] : 0.f;
+    const int h = k / MW, row = k % MW;
+    sqi[h][row] = row < rows_here ? a.qinv[(int64_t)h * n_rows + row0 + row] : 0.f;
   }
-  load(rot, 0);
-  store();
-  __syncthreads();
+  for (int k = tid; k < NW * HR; k += 256) {
+    const int c = k / HR, h = k % HR;
+    sik[h][c] = c < chunks_here ? a.kr_inv_norm[(c0 + c) * HR + h] : 0.f;
+  }
+  const int mydoc = tid < chunks_here ? a.chunk_doc[c0 + tid] : -1;  // document of chunk tid (tid < NW)
+  fill(sA0, sB0, rot, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();  // the scales and the first stage are in LDS
 #pragma unroll 1
   for (int hs = 0; hs < HR; ++hs) {
     const int h = (hs + rot) % HR, hn = (hs + 1 + rot) % HR;
-    float ik[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ik[j] = ikn[j];
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-    load(h, 1);  // second half of this head in flight during the first half's MFMAs
-    multiply(acc);
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (hs + 1 < HR) load(hn, 0);
-    multiply(acc);
+    // first half from buffers 0 while the second half fills buffers 1
+    fill(sA1, sB1, h, 1);
+    multiply(sA0, sB0, acc);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    stage_barrier();
+    // second half from buffers 1 while the next head's first half fills buffers 0
+    if (hs + 1 < HR) fill(sA0, sB0, hn, 0);
+    multiply(sA1, sB1, acc);
     // this head's cosines: acc * (1/H_r)/||q|| (per row) * 1/||k|| (per chunk)
+    float ik[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ik[j] = sik[h][64 * wc + 16 * j + col];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 iq = *reinterpret_cast<const float4 *>(&sqi[h][64 * wr + 16 * i + 4 * G]);
@@ -189,12 +203,11 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
 #pragma unroll
         for (int e = 0; e < 4; ++e) score[i][j][e] = fmaf(acc[i][j][e] * iqe[e], ik[j], score[i][j][e]);
     }
-    __syncthreads();
-    if (hs + 1 < HR) {
-      store();
-      __syncthreads();
-    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    stage_barrier();
   }
+
+  float (*red)[NW] = reinterpret_cast<float (*)[NW]>(sA0);  // per row block: max over its 16 rows
 
   // ---- max over the 16 rows of each row block (rows of one query), per chunk ----
   // score[i][j]: rows 64 wr + 16 i + 4 G + e, chunk 64 wc + 16 j + col
@@ -218,21 +231,24 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
   for (int q = q_first; q <= q_last; ++q) {
     const int rb_lo = (int)std::max<int64_t>(0, ((int64_t)q * a.t_r - row0) / 16);
     const int rb_hi = (int)std::min<int64_t>(MW / 16, ((int64_t)(q + 1) * a.t_r - row0 + 15) / 16);
-    if (tid < NW) {
+    if (tid < NW) {  // waves 0 and 1, one chunk per lane
       float v = -INFINITY;
       for (int i = rb_lo; i < rb_hi; ++i) v = fmaxf(v, red[i][tid]);
-      const int doc = sdoc[tid];
-      if (a.chunk_out && doc >= 0) atomicMax(a.chunk_out + (int64_t)q * a.n_chunks + c0 + tid, score_key(v));
-      // the first chunk of each run of one document reduces the run
-      if (doc >= 0 && (tid == 0 || sdoc[tid - 1] != doc)) {
-        float m = v;
-        for (int j = tid + 1; j < NW && sdoc[j] == doc; ++j) {
-          float w = -INFINITY;
-          for (int i = rb_lo; i < rb_hi; ++i) w = fmaxf(w, red[i][j]);
-          m = fmaxf(m, w);
-        }
-        atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(m));
+      if (a.chunk_out && mydoc >= 0) atomicMax(a.chunk_out + (int64_t)q * a.n_chunks + c0 + tid, score_key(v));
+      // segmented suffix max over the runs of one document within the wave
+      // (chunks of a document are consecutive); every lane takes part in
+      // every shuffle
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float w = __shfl_down(v, o, 64);
+        const int d = __shfl_down(mydoc, o, 64);
+        if (lane + o < 64 && d == mydoc) v = fmaxf(v, w);
       }
+      // the first lane of each run in the wave publishes it (a run crossing the
+      // two waves is published by both halves)
+      const int prev = __shfl_up(mydoc, 1, 64);
+      if (mydoc >= 0 && (lane == 0 || prev != mydoc))
+        atomicMax(a.doc_keys + (int64_t)q * a.n_docs + mydoc, score_key(v));
     }
   }
 }
@@ -250,7 +266,7 @@ hipError_t launch_route_wide(const RouteArgs &a, hipStream_t s) {
   const int n_pairs = n_rows * a.h_r;
   const int64_t threads = (int64_t)n_pairs * (128 / 8);
   hipLaunchKernelGGL(q_inv_norm_kernel<128>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(a.qr), n_pairs, a.h_r, a.qinv);
+                     static_cast<const bf16_t *>(a.qr), n_rows, a.h_r, a.qinv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_mtiles = (n_rows + MW - 1) / MW;
