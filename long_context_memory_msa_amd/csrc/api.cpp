@@ -353,7 +353,10 @@ int msa_topk(const float *s_doc, int32_t n_q, int32_t n_docs, int32_t k, int32_t
     const size_t need = msa::topk_ws_bytes(n_q, n_docs, k);
     if (!ws || ws_bytes < need || !aligned(ws, 16))
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
-    hipError_t e = msa::launch_topk(s_doc, nullptr, n_q, n_docs, k, idx, val, ws, (hipStream_t)stream);
+    msa::TopkSrc src{};
+    src.mode = msa::TopkSrc::SCORES;
+    src.scores = const_cast<float *>(s_doc);  // read only in this mode
+    hipError_t e = msa::launch_topk(src, n_q, n_docs, k, idx, val, ws, (hipStream_t)stream);
     return e == hipSuccess ? ok() : dev_fail(e, "topk");
   } catch (...) {
     return fail(MSA_ERR_DEVICE, "internal error");
@@ -434,8 +437,22 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
       e = rec(0);
       if (e == hipSuccess) e = msa::launch_route_scan(ra, s);
       if (e == hipSuccess) e = rec(1);
-      if (e == hipSuccess) e = msa::launch_resolve_docs(ra, s);
-      if (e == hipSuccess) e = msa::launch_topk(scores, nullptr, n_q, b->n_docs, k, idx, val, tk_ws, s);
+      // documents on tile edges come from the scan's records: a single-pass
+      // top-k resolves them as it loads, the sliced one after a resolve kernel
+      // (coalesced over queries)
+      msa::TopkSrc src{};
+      src.scores = scores;
+      if (msa::topk_single_pass(b->n_docs)) {
+        src.mode = msa::TopkSrc::EDGES;
+        src.edges = ra.edges;
+        src.doc_chunk_off = b->doc_chunk_off;
+        src.n_tiles = (b->n_chunks + 15) / 16;
+        src.t_r = t_r;
+      } else {
+        src.mode = msa::TopkSrc::SCORES;
+        if (e == hipSuccess) e = msa::launch_resolve_docs(ra, s);
+      }
+      if (e == hipSuccess) e = msa::launch_topk(src, n_q, b->n_docs, k, idx, val, tk_ws, s);
       if (e == hipSuccess) e = rec(2);
     } else {
       uint32_t *keys = reinterpret_cast<uint32_t *>(w);
@@ -445,7 +462,10 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
       ra.qinv = static_cast<float *>(rt_ws);
       if (e == hipSuccess) e = msa::launch_route_scan(ra, s);
       if (e == hipSuccess) e = rec(1);
-      if (e == hipSuccess) e = msa::launch_topk(nullptr, keys, n_q, b->n_docs, k, idx, val, tk_ws, s);
+      msa::TopkSrc src{};
+      src.mode = msa::TopkSrc::KEYS;
+      src.keys = keys;
+      if (e == hipSuccess) e = msa::launch_topk(src, n_q, b->n_docs, k, idx, val, tk_ws, s);
       if (e == hipSuccess) e = rec(2);
       if (e == hipSuccess && s_doc) {
         e = hipMemcpyAsync(s_doc, keys, nd * sizeof(uint32_t), hipMemcpyDeviceToDevice, s);

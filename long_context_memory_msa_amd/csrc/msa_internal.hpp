@@ -48,7 +48,7 @@ struct RouteArgs {
   uint32_t *doc_keys;            // [n_q][n_docs]
   // optional per-chunk scores [n_q][n_chunks]: fp32 in single-writer mode, keys otherwise
   uint32_t *chunk_out;
-  // many-row (wide) scan: (1/h_r)/||Q^R|| per query row and head, [n_q * t_r][h_r] (workspace)
+  // many-row (wide) scan: (1/h_r)/||Q^R|| per head and query row, [h_r][n_q * t_r] (workspace)
   float *qinv;
 };
 bool route_single_writer(int t_r);                    // (query, document) scores have one writer
@@ -61,11 +61,47 @@ hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);
 hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s);  // in place
 
+// Score of document `doc` for query `q` in single-writer mode.  The scan stores
+// a document that lies strictly inside one 16-chunk tile itself; for the others
+// it writes per-tile records [row block][tile][first segment 0..15 | last
+// segment 16..31][row], and the document's score is the max of its last
+// segment in the first tile it touches and its first segments in the later ones.
+// Returns false for an interior document (its score is the stored one), else
+// true with the score from the records in *v.
+__device__ __forceinline__ bool edge_doc_score(const float *edges, const int64_t *doc_chunk_off, int64_t n_tiles,
+                                               int t_r, int q, int doc, float *v) {
+  const int rb = t_r == 1 ? q / 16 : q;  // row block of this query
+  const int r = t_r == 1 ? q % 16 : 0;   // its row within the block's records
+  const int64_t c0 = doc_chunk_off[doc], c1 = doc_chunk_off[doc + 1] - 1;
+  const int64_t ta = c0 / 16, tb = c1 / 16;
+  if (ta == tb && (c0 % 16) != 0 && (c1 % 16) != 15) return false;  // interior: stored by the scan
+  const float *rec = edges + (int64_t)rb * n_tiles * 32;
+  float m;
+  if (ta == tb) {
+    m = rec[ta * 32 + ((c0 % 16) == 0 ? 0 : 16) + r];
+  } else {
+    m = rec[ta * 32 + 16 + r];
+    for (int64_t t = ta + 1; t <= tb; ++t) m = fmaxf(m, rec[t * 32 + r]);
+  }
+  *v = m;
+  return true;
+}
+
 // ---- top-k -----------------------------------------------------------------
 size_t topk_ws_bytes(int n_q, int n_docs, int k);
-// scores are either fp32 (keys == nullptr) or order-preserving keys (scores == nullptr)
-hipError_t launch_topk(const float *scores, const uint32_t *keys, int n_q, int n_docs, int k, int32_t *idx,
-                       float *val, void *ws, hipStream_t s);
+bool topk_single_pass(int n_docs);  // one workgroup per query, no workspace
+// Where the document scores [n_q][n_docs] come from
+struct TopkSrc {
+  enum Mode { SCORES = 0, KEYS = 1, EDGES = 2 } mode;
+  float *scores;                 // SCORES: read; EDGES: interior documents read, the others written
+  const uint32_t *keys;          // KEYS: order-preserving keys
+  const float *edges;            // EDGES: the scan's per-tile records
+  const int64_t *doc_chunk_off;  // EDGES
+  int64_t n_tiles;               // EDGES: 16-chunk tiles
+  int t_r;                       // EDGES
+};
+hipError_t launch_topk(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,
+                       hipStream_t s);
 
 // ---- sparse attention ------------------------------------------------------
 struct AttendArgs {

@@ -309,20 +309,9 @@ __global__ void resolve_docs_kernel(const float *edges, const int64_t *doc_chunk
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)n_q * n_docs) return;
   const int q = (int)(i % n_q), doc = (int)(i / n_q);
-  const int rb = t_r == 1 ? q / 16 : q;          // row block of this query
-  const int r = t_r == 1 ? q % 16 : 0;           // its row within the block's records
-  const int64_t c0 = doc_chunk_off[doc], c1 = doc_chunk_off[doc + 1] - 1;
-  const int64_t ta = c0 / 16, tb = c1 / 16;
-  if (ta == tb && (c0 % 16) != 0 && (c1 % 16) != 15) return;  // interior: already stored
-  const float *rec = edges + (int64_t)rb * n_tiles * 32;
+  float *out = doc_scores + (int64_t)q * n_docs + doc;
   float v;
-  if (ta == tb) {
-    v = rec[ta * 32 + ((c0 % 16) == 0 ? 0 : 16) + r];
-  } else {
-    v = rec[ta * 32 + 16 + r];
-    for (int64_t t = ta + 1; t <= tb; ++t) v = fmaxf(v, rec[t * 32 + r]);
-  }
-  doc_scores[(int64_t)q * n_docs + doc] = v;
+  if (edge_doc_score(edges, doc_chunk_off, n_tiles, t_r, q, doc, &v)) *out = v;
 }
 
 template <typename T, int HR, int DR, bool EDGE>

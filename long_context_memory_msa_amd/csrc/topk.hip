@@ -6,15 +6,18 @@
 //   (order-preserving score key << 32) | (0xFFFFFFFF - doc)
 // so "larger composite" is exactly "higher score, then lower index": the
 // selection is unique and independent of thread order.
-//   pass 1: one workgroup per (query, slice of 2048 documents) finds the
-//           slice's top-k composites by an 8-bit radix select (MSB first,
+//   pass 1: one workgroup per (query, slice of 2048 documents) holds the
+//           slice in registers (8 composites per thread) and finds its top-k
+//           by an 8-bit radix select (MSB first, per-wave LDS histograms,
 //           stopping as soon as the boundary digit bin is taken whole);
 //   pass 2: one workgroup per query selects the top-k of the candidates
 //           the same way and sorts them (bitonic, in LDS).
 // Up to 8K documents per query a single pass does it all: one 1024-thread
 // workgroup per query holds the whole row in registers (24 composites per
-// thread), radix-selects with per-wave LDS histograms, compacts the k winners
-// and sorts them.
+// thread), selects, compacts the k winners and sorts them.
+// The scores are read as fp32, as order-preserving keys, or resolved from the
+// router scan's per-tile records (single-writer scan: the documents that
+// touch a tile edge are resolved here, and stored, while loading).
 #include <algorithm>
 
 #include "msa_device.hpp"
@@ -141,40 +144,6 @@ __device__ void radix_select(Get get, int64_t n, uint32_t need, SelShared &sh, i
   *out_prefix = prefix;
 }
 
-template <bool FROM_KEYS>
-__global__ __launch_bounds__(TK_THREADS) void topk_pass1(const float *scores, const uint32_t *keys, int n_docs, int k,
-                                                           int n_slices, uint64_t *cand) {
-  __shared__ SelShared sh;
-  const int q = blockIdx.y, slice = blockIdx.x;
-  const int64_t lo = (int64_t)slice * TK_SLICE;
-  const int64_t n = std::min<int64_t>(TK_SLICE, n_docs - lo);
-  const uint32_t kk = (uint32_t)std::min<int64_t>(k, n);
-  const int64_t rowbase = (int64_t)q * n_docs + lo;
-  auto get = [&](int64_t i) -> uint64_t {
-    const uint32_t key = FROM_KEYS ? keys[rowbase + i] : score_key(scores[rowbase + i]);
-    return composite(key, lo + i);
-  };
-  int shift;
-  uint64_t prefix;
-  radix_select(get, n, kk, sh, &shift, &prefix);
-  uint64_t *out = cand + ((int64_t)q * n_slices + slice) * k;
-  // compaction in index order (items per thread are strided by the block size)
-  for (int64_t base = 0; base < n; base += TK_THREADS) {
-    const int64_t i = base + threadIdx.x;
-    uint64_t v = 0;
-    int f = 0;
-    if (i < n) {
-      v = get(i);
-      f = (v >> shift) >= (prefix >> shift);
-    }
-    int tot;
-    const int pos = block_excl_scan(f, sh, &tot);
-    if (f) out[pos] = v;
-    out += tot;
-  }
-  for (int j = kk + threadIdx.x; j < k; j += TK_THREADS) cand[((int64_t)q * n_slices + slice) * k + j] = 0;
-}
-
 __global__ __launch_bounds__(TK_THREADS) void topk_pass2(const uint64_t *cand, int64_t n_cand, int k, int kpad,
                                                            int32_t *idx, float *val) {
   __shared__ SelShared sh;
@@ -226,56 +195,65 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass2(const uint64_t *cand, i
   }
 }
 
-// ---- single pass: one 1024-thread workgroup per query ---------------------
-constexpr int TS_THREADS = 1024;
-constexpr int TS_ITEMS = 24;
-constexpr int TS_WAVES = TS_THREADS / 64;
-
-struct SingleShared {
-  uint32_t hist[TS_WAVES][256];   // per-wave histograms
+// ---- selection over register-resident composites ------------------------------
+template <int WAVES>
+struct RegShared {
+  uint32_t hist[WAVES][256];  // per-wave histograms
   uint32_t total[256];
-  int32_t wave_tot[TS_WAVES];
+  int32_t wave_tot[WAVES];
   uint32_t bin, above, in_bin;
-  uint64_t sel[TK_MAX_K];
 };
 
-template <bool FROM_KEYS>
-__global__ __launch_bounds__(TS_THREADS) void topk_single(const float *scores, const uint32_t *keys, int n_docs,
-                                                             int k, int kpad, int32_t *idx, float *val) {
-  __shared__ SingleShared sh;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = (int64_t)q * n_docs;
-  uint64_t v[TS_ITEMS];
-#pragma unroll
-  for (int j = 0; j < TS_ITEMS; ++j) {
-    const int i = j * TS_THREADS + tid;  // coalesced
-    uint64_t x = 0;
-    if (i < n_docs) x = composite(FROM_KEYS ? keys[row + i] : score_key(scores[row + i]), i);
-    v[j] = x;
+// Composite of document `doc` (< n_docs) for query q from the score source.
+template <int MODE>
+__device__ __forceinline__ uint64_t load_composite(const TopkSrc &src, int q, int n_docs, int doc) {
+  const int64_t at = (int64_t)q * n_docs + doc;
+  uint32_t key;
+  if constexpr (MODE == TopkSrc::KEYS) {
+    key = src.keys[at];
+  } else if constexpr (MODE == TopkSrc::SCORES) {
+    key = score_key(src.scores[at]);
+  } else {
+    float v;
+    if (edge_doc_score(src.edges, src.doc_chunk_off, src.n_tiles, src.t_r, q, doc, &v))
+      src.scores[at] = v;  // complete the document scores for the caller
+    else
+      v = src.scores[at];
+    key = score_key(v);
   }
-  // radix select, MSB first, 8 bits per pass, stopping when the boundary bin is taken whole
+  return composite(key, doc);
+}
+
+// Radix select of the `need` largest nonzero composites held ITEMS per thread
+// by a THREADS-wide workgroup.  Returns (shift, prefix): the selected are the v
+// with (v >> shift) >= (prefix >> shift), exactly `need` of them.
+template <int ITEMS, int THREADS>
+__device__ void select_regs(const uint64_t (&v)[ITEMS], uint32_t need, RegShared<THREADS / 64> &sh, int *out_shift,
+                            uint64_t *out_prefix) {
+  constexpr int WAVES = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t prefix = 0;
-  uint32_t need = (uint32_t)k;
   int shift = 56;
   for (;; shift -= 8) {
-    for (int e = tid; e < TS_WAVES * 256; e += TS_THREADS) (&sh.hist[0][0])[e] = 0;
+    for (int e = tid; e < WAVES * 256; e += THREADS) (&sh.hist[0][0])[e] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < TS_ITEMS; ++j) {
+    for (int j = 0; j < ITEMS; ++j) {
       const bool match = v[j] != 0 && ((shift == 56) || ((v[j] ^ prefix) >> (shift + 8)) == 0);
       const uint32_t digit = (uint32_t)(v[j] >> shift) & 255;
       if (shift == 56) hist_add_wave(sh.hist[wave], digit, match);
       else if (match) atomicAdd(&sh.hist[wave][digit], 1u);
     }
     __syncthreads();
-    if (tid < 256) {
+    for (int b = tid; b < 256; b += THREADS) {
       uint32_t t = 0;
 #pragma unroll
-      for (int w = 0; w < TS_WAVES; ++w) t += sh.hist[w][tid];
-      sh.total[tid] = t;
+      for (int w = 0; w < WAVES; ++w) t += sh.hist[w][b];
+      sh.total[b] = t;
     }
     __syncthreads();
     if (wave == 0) {
+      // lane l owns bins 255-4l .. 252-4l (descending digit order)
       uint32_t c[4], s = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -310,10 +288,19 @@ __global__ __launch_bounds__(TS_THREADS) void topk_single(const float *scores, c
     need -= above;
     if (in_bin == need || shift == 0) break;
   }
-  // compact the k winners into LDS (positions from a block prefix sum), then sort
+  *out_shift = shift;
+  *out_prefix = prefix;
+}
+
+// Writes the selected composites to out[0 ..) (in thread order); returns their number.
+template <int ITEMS, int THREADS>
+__device__ int compact_regs(const uint64_t (&v)[ITEMS], int shift, uint64_t prefix, RegShared<THREADS / 64> &sh,
+                            uint64_t *out) {
+  constexpr int WAVES = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < TS_ITEMS; ++j) cnt += (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift));
+  for (int j = 0; j < ITEMS; ++j) cnt += (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift));
   int x = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -321,24 +308,77 @@ __global__ __launch_bounds__(TS_THREADS) void topk_single(const float *scores, c
     if (lane >= o) x += y;
   }
   if (lane == 63) sh.wave_tot[wave] = x;
-  for (int e = tid; e < kpad; e += TS_THREADS) sh.sel[e] = 0;
   __syncthreads();
-  int pos = x - cnt;
-  for (int w = 0; w < wave; ++w) pos += sh.wave_tot[w];
+  int pos = x - cnt, total = 0;
 #pragma unroll
-  for (int j = 0; j < TS_ITEMS; ++j)
-    if (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift)) sh.sel[pos++] = v[j];
+  for (int w = 0; w < WAVES; ++w) {
+    if (w < wave) pos += sh.wave_tot[w];
+    total += sh.wave_tot[w];
+  }
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift)) out[pos++] = v[j];
+  return total;
+}
+
+// ---- pass 1: the top-k of each (query, slice) ------------------------------------
+constexpr int P1_ITEMS = TK_SLICE / TK_THREADS;
+
+template <int MODE>
+__global__ __launch_bounds__(TK_THREADS) void topk_pass1(TopkSrc src, int n_docs, int k, int n_slices,
+                                                           uint64_t *cand) {
+  __shared__ RegShared<TK_THREADS / 64> sh;
+  const int q = blockIdx.y, slice = blockIdx.x, tid = threadIdx.x;
+  const int lo = slice * TK_SLICE;
+  const int n = std::min(TK_SLICE, n_docs - lo);
+  const uint32_t kk = (uint32_t)std::min(k, n);
+  uint64_t v[P1_ITEMS];
+#pragma unroll
+  for (int j = 0; j < P1_ITEMS; ++j) {
+    const int i = j * TK_THREADS + tid;  // coalesced
+    v[j] = i < n ? load_composite<MODE>(src, q, n_docs, lo + i) : 0;
+  }
+  int shift;
+  uint64_t prefix;
+  select_regs<P1_ITEMS, TK_THREADS>(v, kk, sh, &shift, &prefix);
+  uint64_t *out = cand + ((int64_t)q * n_slices + slice) * k;
+  compact_regs<P1_ITEMS, TK_THREADS>(v, shift, prefix, sh, out);
+  for (int j = kk + tid; j < k; j += TK_THREADS) out[j] = 0;
+}
+
+// ---- single pass: one 1024-thread workgroup per query ---------------------
+constexpr int TS_THREADS = 1024;
+constexpr int TS_ITEMS = 24;
+
+template <int MODE>
+__global__ __launch_bounds__(TS_THREADS) void topk_single(TopkSrc src, int n_docs, int k, int kpad, int32_t *idx,
+                                                             float *val) {
+  __shared__ RegShared<TS_THREADS / 64> sh;
+  __shared__ uint64_t sel[TK_MAX_K];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  uint64_t v[TS_ITEMS];
+#pragma unroll
+  for (int j = 0; j < TS_ITEMS; ++j) {
+    const int i = j * TS_THREADS + tid;  // coalesced
+    v[j] = i < n_docs ? load_composite<MODE>(src, q, n_docs, i) : 0;
+  }
+  int shift;
+  uint64_t prefix;
+  select_regs<TS_ITEMS, TS_THREADS>(v, (uint32_t)k, sh, &shift, &prefix);
+  for (int e = tid; e < kpad; e += TS_THREADS) sel[e] = 0;
+  __syncthreads();
+  compact_regs<TS_ITEMS, TS_THREADS>(v, shift, prefix, sh, sel);
   __syncthreads();
   for (int size = 2; size <= kpad; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (tid < kpad) {
         const int j = tid ^ stride;
         if (j > tid) {
-          const uint64_t a = sh.sel[tid], b = sh.sel[j];
+          const uint64_t a = sel[tid], b = sel[j];
           const bool desc = (tid & size) == 0;
           if (desc ? (a < b) : (a > b)) {
-            sh.sel[tid] = b;
-            sh.sel[j] = a;
+            sel[tid] = b;
+            sel[j] = a;
           }
         }
       }
@@ -346,7 +386,7 @@ __global__ __launch_bounds__(TS_THREADS) void topk_single(const float *scores, c
     }
   }
   if (tid < k) {
-    const uint64_t w64 = sh.sel[tid];
+    const uint64_t w64 = sel[tid];
     idx[(int64_t)q * k + tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)w64);
     val[(int64_t)q * k + tid] = key_score((uint32_t)(w64 >> 32));
   }
@@ -363,29 +403,31 @@ size_t topk_ws_bytes(int n_q, int n_docs, int k) {
   return (size_t)n_q * n_slices_for(n_docs) * k * sizeof(uint64_t);
 }
 
-hipError_t launch_topk(const float *scores, const uint32_t *keys, int n_q, int n_docs, int k, int32_t *idx, float *val,
-                       void *ws, hipStream_t s) {
+template <int MODE>
+hipError_t topk_launch(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,
+                       hipStream_t s) {
   int kpad = 1;
   while (kpad < k) kpad <<= 1;
   if (topk_single_pass(n_docs)) {
-    if (keys)
-      hipLaunchKernelGGL(topk_single<true>, dim3(n_q), dim3(TS_THREADS), 0, s, scores, keys, n_docs, k, kpad, idx, val);
-    else
-      hipLaunchKernelGGL(topk_single<false>, dim3(n_q), dim3(TS_THREADS), 0, s, scores, keys, n_docs, k, kpad, idx,
-                         val);
+    hipLaunchKernelGGL(topk_single<MODE>, dim3(n_q), dim3(TS_THREADS), 0, s, src, n_docs, k, kpad, idx, val);
     return hipGetLastError();
   }
   const int ns = n_slices_for(n_docs);
   uint64_t *cand = static_cast<uint64_t *>(ws);
-  dim3 g1(ns, n_q);
-  if (keys)
-    hipLaunchKernelGGL(topk_pass1<true>, g1, dim3(TK_THREADS), 0, s, scores, keys, n_docs, k, ns, cand);
-  else
-    hipLaunchKernelGGL(topk_pass1<false>, g1, dim3(TK_THREADS), 0, s, scores, keys, n_docs, k, ns, cand);
+  hipLaunchKernelGGL(topk_pass1<MODE>, dim3(ns, n_q), dim3(TK_THREADS), 0, s, src, n_docs, k, ns, cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_pass2, dim3(n_q), dim3(TK_THREADS), 0, s, cand, (int64_t)ns * k, k, kpad, idx, val);
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,
+                       hipStream_t s) {
+  switch (src.mode) {
+    case TopkSrc::SCORES: return topk_launch<TopkSrc::SCORES>(src, n_q, n_docs, k, idx, val, ws, s);
+    case TopkSrc::KEYS: return topk_launch<TopkSrc::KEYS>(src, n_q, n_docs, k, idx, val, ws, s);
+    default: return topk_launch<TopkSrc::EDGES>(src, n_q, n_docs, k, idx, val, ws, s);
+  }
 }
 
 }  // namespace msa
