@@ -141,6 +141,37 @@ def test_route_isolated(device, name, t_r, n_q):
     assert torch.equal(s_doc, s_doc2)
 
 
+# every router head shape the ABI admits (h_r in 1..16, d_r 64 / 128, fp32 and
+# bf16), few rows (decode scan) and many rows per query (tiled scan), on a small
+# ragged bank of the prefill workload's document law (several 128-chunk tiles)
+@pytest.mark.parametrize("dtype,h_r,d_r,t_r,n_q", [
+    ("bf16", 1, 128, 48, 2), ("bf16", 2, 128, 32, 3), ("bf16", 4, 128, 64, 1), ("bf16", 2, 128, 1, 16),
+    ("bf16", 4, 64, 1, 5), ("bf16", 16, 64, 32, 2), ("bf16", 16, 64, 1, 16), ("f32", 16, 64, 16, 1),
+    ("f32", 4, 128, 5, 2), ("f32", 8, 128, 48, 1)])
+def test_route_head_shapes(device, dtype, h_r, d_r, t_r, n_q):
+    w = _wl(2, 60_000)
+    # one small attention head: K/V do not enter the routing
+    w = dataclasses.replace(w, dtype=dtype, h_r=h_r, d_r=d_r, h_kv=1, d=64, h_q=1, n_q=n_q,
+                            gold=np.zeros((n_q, 0), np.int64))
+    log(f"route shapes {dtype} h_r={h_r} d_r={d_r} t_r={t_r} n_q={n_q} chunks={w.n_chunks}")
+    qi = W.query_inputs(w)
+    KR = W.bank_raw(w, rng.ROLE_KR, 0, w.n_tok)
+    zeros = np.zeros((w.n_tok, w.h_kv, w.d), np.float32)
+    ob = O.pool(w.doc_lens, w.chunk, zeros, zeros, KR, w.dtype, w.rope_base)
+    QRh = qi["QR"][:, :t_r]
+    S = O.chunk_scores(QRh, ob["krbar"])
+    sd = O.doc_scores(S, ob["doc_chunk_off"])
+    bank, _ = gpu_bank_from_oracle(w, ob, device)
+    s_doc = torch.empty((n_q, w.n_docs), dtype=torch.float32, device=device)
+    s_chunk = torch.empty((n_q, w.n_chunks), dtype=torch.float32, device=device)
+    nb = L.msa_route_workspace_bytes(bank.c, n_q, t_r)
+    ws = M.workspace(nb, device)
+    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc, s_chunk, ws, nb)
+    torch.cuda.synchronize()
+    assert np.abs(host(s_chunk) - S).max() <= 2e-3
+    assert np.abs(host(s_doc) - sd).max() <= 2e-3
+
+
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n_q,n_docs,k", [(1, 7, 1), (1, 7, 7), (3, 2048, 16), (2, 5000, 256), (16, 23048, 16),
                                           (4, 4099, 64), (1, 300, 256), (1, 24576, 256),
