@@ -89,9 +89,20 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
     const T *qp = static_cast<const T *>(a.Q) + (((int64_t)q * a.T + t) * a.h_q + h) * D;
     float x[KS][EL];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (EL == 8) {  // bf16: one 16-byte load per k-step
+        const uint4 w = row_ok ? *reinterpret_cast<const uint4 *>(qp + s * KW + G * EL) : uint4{0u, 0u, 0u, 0u};
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int e = 0; e < EL; ++e) x[s][e] = row_ok ? Elem<T>::to_f32(qp[s * KW + G * EL + e]) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          x[s][2 * e] = __uint_as_float(ws[e] << 16);
+          x[s][2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) x[s][e] = row_ok ? Elem<T>::to_f32(qp[s * KW + G * EL + e]) : 0.f;
+      }
+    }
     const int64_t crow = (int64_t)(a.pos0 + s_t) * (D / 2);
 #pragma unroll
     for (int s = 0; s < KS / 2; ++s)
@@ -213,6 +224,26 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       const int u = threadIdx.x + i * NT;
       if (u >= KT * NP) continue;
       const int key = u / NP, m = u % NP;
+      if constexpr (sizeof(T) == 2) {
+        if (rpos[i] < 0) {
+          // pooled (or zero) bf16 key: the words go to LDS as they are; V^T
+          // takes each 16-bit element straight from its word
+          *reinterpret_cast<uint4 *>(sK + key * KROW + m * EPS) = rk[i][0];
+          *reinterpret_cast<uint4 *>(sK + key * KROW + D / 2 + m * EPS) = rk[i][1];
+          uint16_t *v16 = reinterpret_cast<uint16_t *>(sV);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const uint32_t wv[4] = {rv[i][p].x, rv[i][p].y, rv[i][p].z, rv[i][p].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int dim = p * (D / 2) + m * EPS + 2 * e;
+              v16[dim * VROW + key] = (uint16_t)(wv[e] & 0xFFFFu);
+              v16[(dim + 1) * VROW + key] = (uint16_t)(wv[e] >> 16);
+            }
+          }
+          continue;
+        }
+      }
       float lo[EPS], hi[EPS], vlo[EPS], vhi[EPS];
       float *dk[2] = {lo, hi}, *dv[2] = {vlo, vhi};
 #pragma unroll
