@@ -6,12 +6,14 @@
 //   (order-preserving score key << 32) | (0xFFFFFFFF - doc)
 // so "larger composite" is exactly "higher score, then lower index": the
 // selection is unique and independent of thread order.
-//   pass 1: one workgroup per (query, slice of 2048 documents) holds the
-//           slice in registers (8 composites per thread) and finds its top-k
-//           by an 8-bit radix select (MSB first, per-wave LDS histograms,
-//           stopping as soon as the boundary digit bin is taken whole);
+//   pass 1: the top-k of each (query, slice) by an 8-bit radix select held in
+//           registers (MSB first, stopping as soon as the boundary digit bin is
+//           taken whole): for k <= 32 one wave per slice of 512 documents (its
+//           own LDS histogram and shuffles, no workgroup barrier), else one
+//           256-thread workgroup per slice of 2048 (per-wave histograms);
 //   pass 2: one workgroup per query selects the top-k of the candidates
-//           the same way and sorts them (bitonic, in LDS).
+//           the same way (from registers when they fit, 2048 per query) and
+//           sorts them (bitonic, in LDS).
 // Up to 8K documents per query a single pass does it all: one 1024-thread
 // workgroup per query holds the whole row in registers (24 composites per
 // thread), selects, compacts the k winners and sorts them.
@@ -44,17 +46,23 @@ struct SelShared {
 #endif
 
 // Histogram add for a digit that most lanes share (the first, sign/exponent
-// digit of cosine scores): one LDS atomic per distinct digit in the wave
-// instead of one per lane.  Every lane of the wave must call it.
+// digit of cosine scores): the two digits met first in the wave are added with
+// one LDS atomic each, the remaining lanes add one by one.  (An exhaustive
+// loop over distinct digits costs one shuffle round trip per digit; scores
+// spread over several binades made it slower than plain atomics.)  Every lane
+// of the wave must call it.
 __device__ __forceinline__ void hist_add_wave(uint32_t *hist, uint32_t digit, bool active) {
   unsigned long long pending = __ballot(active);
-  while (pending) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (!pending) break;
     const int leader = __ffsll((long long)pending) - 1;
     const uint32_t d = __shfl(digit, leader, 64);
     const unsigned long long same = __ballot(active && digit == d);
     if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[d], (uint32_t)__popcll(same));
     pending &= ~same;
   }
+  if ((pending >> (threadIdx.x & 63)) & 1ull) atomicAdd(&hist[digit], 1u);
 }
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int64_t i) {
@@ -346,6 +354,162 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass1(TopkSrc src, int n_docs
   for (int j = kk + tid; j < k; j += TK_THREADS) out[j] = 0;
 }
 
+// ---- pass 1 for small k: one wave per (query, slice of 512 documents) ---------
+// Each wave selects on its own, with its own LDS histogram and shuffles: no
+// workgroup barrier, so a radix pass costs a few LDS round trips.
+constexpr int WS_SLICE = 512;
+constexpr int WS_ITEMS = WS_SLICE / 64;
+constexpr int WS_MAX_K = 32;  // k up to this uses the wave pass (k <= slice / 16)
+
+// orders this wave's LDS accesses before and after it (LDS executes a wave's
+// operations in order; this keeps the compiler from moving them across)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int ITEMS>
+__device__ void select_wave(const uint64_t (&v)[ITEMS], uint32_t need, uint32_t *hist, int *out_shift,
+                            uint64_t *out_prefix) {
+  const int lane = threadIdx.x & 63;
+  uint64_t prefix = 0;
+  int shift = 56;
+  for (;; shift -= 8) {
+    reinterpret_cast<uint4 *>(hist)[lane] = uint4{0u, 0u, 0u, 0u};
+    wave_sync();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const bool match = v[j] != 0 && ((shift == 56) || ((v[j] ^ prefix) >> (shift + 8)) == 0);
+      const uint32_t digit = (uint32_t)(v[j] >> shift) & 255;
+      if (shift == 56) hist_add_wave(hist, digit, match);
+      else if (match) atomicAdd(&hist[digit], 1u);
+    }
+    wave_sync();
+    // lane l owns bins 255-4l .. 252-4l (descending digit order)
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = hist[255 - 4 * lane - j];
+      sum += c[j];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const unsigned long long m = __ballot(incl >= need);
+    const int first = __ffsll((long long)m) - 1;
+    uint32_t bin = 0, above = 0, in_bin = 0;
+    {
+      uint32_t cum = incl - sum;
+      bool found = false;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!found && cum + c[j] >= need) {
+          bin = 255 - 4 * lane - j;
+          above = cum;
+          in_bin = c[j];
+          found = true;
+        }
+        cum += c[j];
+      }
+    }
+    bin = __shfl(bin, first, 64);
+    above = __shfl(above, first, 64);
+    in_bin = __shfl(in_bin, first, 64);
+    wave_sync();  // the histogram is read before the next pass clears it
+    prefix |= (uint64_t)bin << shift;
+    need -= above;
+    if (in_bin == need || shift == 0) break;
+  }
+  *out_shift = shift;
+  *out_prefix = prefix;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, int k, int n_slices,
+                                                        uint64_t *cand) {
+  __shared__ __align__(16) uint32_t hist[4][256];
+  const int q = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slice = blockIdx.x * 4 + wave;
+  if (slice >= n_slices) return;  // whole wave; no workgroup barrier below
+  const int lo = slice * WS_SLICE;
+  const int n = std::min(WS_SLICE, n_docs - lo);
+  const uint32_t kk = (uint32_t)std::min(k, n);
+  uint64_t v[WS_ITEMS];
+#pragma unroll
+  for (int j = 0; j < WS_ITEMS; ++j) {
+    const int i = j * 64 + lane;  // coalesced
+    v[j] = i < n ? load_composite<MODE>(src, q, n_docs, lo + i) : 0;
+  }
+  int shift;
+  uint64_t prefix;
+  select_wave<WS_ITEMS>(v, kk, hist[wave], &shift, &prefix);
+  uint64_t *out = cand + ((int64_t)q * n_slices + slice) * k;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < WS_ITEMS; ++j) cnt += (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift));
+  int x = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  int pos = x - cnt;
+#pragma unroll
+  for (int j = 0; j < WS_ITEMS; ++j)
+    if (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift)) out[pos++] = v[j];
+  for (int j = (int)kk + lane; j < k; j += 64) out[j] = 0;
+}
+
+// ---- pass 2 over register-resident candidates (up to 8 per thread) ----------
+constexpr int P2_THREADS = 256;
+constexpr int P2_ITEMS = 8;
+
+__global__ __launch_bounds__(P2_THREADS) void topk_pass2_regs(const uint64_t *cand, int n_cand, int k, int kpad,
+                                                                int32_t *idx, float *val) {
+  __shared__ RegShared<P2_THREADS / 64> sh;
+  __shared__ uint64_t sel[TK_MAX_K];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const uint64_t *c = cand + (int64_t)q * n_cand;
+  uint64_t v[P2_ITEMS];
+#pragma unroll
+  for (int j = 0; j < P2_ITEMS; ++j) {
+    const int i = j * P2_THREADS + tid;
+    v[j] = i < n_cand ? c[i] : 0;  // empty candidate slots are 0
+  }
+  int shift;
+  uint64_t prefix;
+  select_regs<P2_ITEMS, P2_THREADS>(v, (uint32_t)k, sh, &shift, &prefix);
+  for (int e = tid; e < kpad; e += P2_THREADS) sel[e] = 0;
+  __syncthreads();
+  compact_regs<P2_ITEMS, P2_THREADS>(v, shift, prefix, sh, sel);
+  __syncthreads();
+  for (int size = 2; size <= kpad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (tid < kpad) {
+        const int j = tid ^ stride;
+        if (j > tid) {
+          const uint64_t a = sel[tid], b = sel[j];
+          const bool desc = (tid & size) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            sel[tid] = b;
+            sel[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < k) {
+    const uint64_t w64 = sel[tid];
+    idx[(int64_t)q * k + tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)w64);
+    val[(int64_t)q * k + tid] = key_score((uint32_t)(w64 >> 32));
+  }
+}
+
 // ---- single pass: one 1024-thread workgroup per query ---------------------
 constexpr int TS_THREADS = 1024;
 constexpr int TS_ITEMS = 24;
@@ -392,7 +556,9 @@ __global__ __launch_bounds__(TS_THREADS) void topk_single(TopkSrc src, int n_doc
   }
 }
 
-int n_slices_for(int n_docs) { return (n_docs + TK_SLICE - 1) / TK_SLICE; }
+// documents per pass-1 slice: 512 (one wave) for small k, else 2048 (one workgroup)
+int slice_for(int k) { return k <= WS_MAX_K ? WS_SLICE : TK_SLICE; }
+int n_slices_for(int n_docs, int k) { return (n_docs + slice_for(k) - 1) / slice_for(k); }
 
 }  // namespace
 
@@ -400,7 +566,7 @@ bool topk_single_pass(int n_docs) { return n_docs <= TS_THREADS * TS_ITEMS && n_
 
 size_t topk_ws_bytes(int n_q, int n_docs, int k) {
   if (topk_single_pass(n_docs)) return 0;
-  return (size_t)n_q * n_slices_for(n_docs) * k * sizeof(uint64_t);
+  return (size_t)n_q * n_slices_for(n_docs, k) * k * sizeof(uint64_t);
 }
 
 template <int MODE>
@@ -412,12 +578,19 @@ hipError_t topk_launch(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *
     hipLaunchKernelGGL(topk_single<MODE>, dim3(n_q), dim3(TS_THREADS), 0, s, src, n_docs, k, kpad, idx, val);
     return hipGetLastError();
   }
-  const int ns = n_slices_for(n_docs);
+  const int ns = n_slices_for(n_docs, k);
   uint64_t *cand = static_cast<uint64_t *>(ws);
-  hipLaunchKernelGGL(topk_pass1<MODE>, dim3(ns, n_q), dim3(TK_THREADS), 0, s, src, n_docs, k, ns, cand);
+  if (slice_for(k) == WS_SLICE)
+    hipLaunchKernelGGL(topk_pass1_wave<MODE>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k, ns, cand);
+  else
+    hipLaunchKernelGGL(topk_pass1<MODE>, dim3(ns, n_q), dim3(TK_THREADS), 0, s, src, n_docs, k, ns, cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_pass2, dim3(n_q), dim3(TK_THREADS), 0, s, cand, (int64_t)ns * k, k, kpad, idx, val);
+  const int64_t n_cand = (int64_t)ns * k;
+  if (n_cand <= (int64_t)P2_THREADS * P2_ITEMS)
+    hipLaunchKernelGGL(topk_pass2_regs, dim3(n_q), dim3(P2_THREADS), 0, s, cand, (int)n_cand, k, kpad, idx, val);
+  else
+    hipLaunchKernelGGL(topk_pass2, dim3(n_q), dim3(TK_THREADS), 0, s, cand, n_cand, k, kpad, idx, val);
   return hipGetLastError();
 }
 

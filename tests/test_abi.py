@@ -109,7 +109,8 @@ def test_route_validation():
 
 def test_topk_validation_and_workspace():
     assert msa.msa_topk_workspace_bytes(2, 5000, 16) == 0                 # one pass per query
-    assert msa.msa_topk_workspace_bytes(2, 20000, 16) == 2 * 10 * 16 * 8  # 2048-document slices
+    assert msa.msa_topk_workspace_bytes(2, 20000, 16) == 2 * 40 * 16 * 8    # k <= 32: 512-document slices
+    assert msa.msa_topk_workspace_bytes(2, 20000, 64) == 2 * 10 * 64 * 8    # larger k: 2048-document slices
     assert msa.msa_topk_workspace_bytes(1, 10, 11) == 0
     assert _code(msa.msa_topk, A, 1, 10, 11, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG      # k > n_docs
     assert _code(msa.msa_topk, A, 1, 1000, 257, A, A, A, 1 << 20, 0) == L.MSA_ERR_ARG   # k > 256
