@@ -38,7 +38,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int MW = 128;  // rows per workgroup
-constexpr int NW = 128;  // chunks per workgroup
+// chunks per workgroup (a compile-time knob: 128 -> 4 waves, 256 -> 8 waves)
+#ifndef MSA_WIDE_NW
+#define MSA_WIDE_NW 128
+#endif
+constexpr int WIDE_NW = MSA_WIDE_NW;
 
 // qinv[h][row] = (1/H_r) / ||Q^R[row][h]|| (0 for a zero row); 16 lanes per (row, head)
 template <int DR>
@@ -69,6 +73,12 @@ __global__ void q_inv_norm_kernel(const bf16_t *qr, int n_rows, int h_r, float *
 // eight different bank groups, so fragment reads of 16 rows are conflict-free.
 __device__ __forceinline__ int slot_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// 16-byte direct-to-LDS load: this lane's 16 bytes at g land at lds_base +
+// 16 * lane (lds_base is wave-uniform)
+__device__ __forceinline__ void lds_fill16(const bf16_t *g, bf16_t *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
+}
+
 // s_waitcnt immediates (gfx9 encoding): wait until at most N vector-memory
 // operations of this wave are outstanding, leaving the other counters alone
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -83,11 +93,14 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-template <int HR, int DR>
-__global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_mtiles, int64_t n_ntiles) {
+template <int HR, int DR, int NW>
+__global__ __launch_bounds__(2 * NW, 2) void route_wide_kernel(RouteArgs a, int n_mtiles, int64_t n_ntiles) {
   static_assert(DR == 128, "stage layout assumes 128-dim router heads");
   constexpr int SD = DR / 2;       // one stage = half of a head's dimensions (128 bytes per row)
-  constexpr int FILLS = 4;         // direct-to-LDS loads per wave per operand per stage
+  constexpr int NT = 2 * NW;       // threads: 2 x (NW / 64) waves of 64 rows x 64 chunks
+  constexpr int WAVES = NT / 64;
+  constexpr int FA = MW / WAVES / 8;  // direct-to-LDS loads per wave per stage: query rows
+  constexpr int FB = NW / WAVES / 8;  //                                          chunk rows
   // Stage buffers (rows of 128 bytes, slots swizzled, filled by direct-to-LDS
   // loads), double-buffered: buffers 0 hold the first half of a head, buffers
   // 1 the second.  Each buffer is its own variable so that the compiler can
@@ -107,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, G = lane >> 4;
-  const int wr = wave >> 1, wc = wave & 1;  // 2 x 2 waves of 64 rows x 64 chunks
+  const int wr = wave & 1, wc = wave >> 1;  // waves of 64 rows x 64 chunks
   const int n_rows = a.n_q * a.t_r;
   const int64_t row0 = (int64_t)m_tile * MW, c0 = n_tile * NW;
   const int rows_here = (int)std::min<int64_t>(MW, n_rows - row0);
@@ -116,25 +129,30 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
   const bf16_t *kt = static_cast<const bf16_t *>(a.krbar) + c0 * HR * DR;   // this tile's chunks
   const int rot = (int)(n_tile % HR);
 
-  // Fill of a stage: wave w writes rows 32w .. 32w+31 with four loads; in load
-  // p, lane L writes row 32w + 8p + L/8 at physical slot L%8, which holds the
-  // logical slot (L%8) ^ slot_swz(row).  Rows and chunks past the end read the
-  // last valid one (clamped, no branch); the epilogue discards them.
-  uint32_t aoff[FILLS], boff[FILLS];
+  // Fill of a stage: wave w writes its share of the rows (MW / WAVES query rows,
+  // NW / WAVES chunk rows) with 16-byte direct-to-LDS loads; in load p, lane L
+  // writes row base + 8p + L/8 at physical slot L%8, which holds the logical
+  // slot (L%8) ^ slot_swz(row).  Rows and chunks past the end read the last
+  // valid one (clamped, no branch); the epilogue discards them.
+  uint32_t aoff[FA], boff[FB];
 #pragma unroll
-  for (int p = 0; p < FILLS; ++p) {
-    const int row = 32 * wave + 8 * p + lane / 8;
-    const int slot = (lane % 8) ^ slot_swz(row);
-    aoff[p] = (uint32_t)(std::min(row, rows_here - 1) * HR * DR + slot * 8);
-    boff[p] = (uint32_t)(std::min(row, chunks_here - 1) * HR * DR + slot * 8);
+  for (int p = 0; p < FA; ++p) {
+    const int row = (MW / WAVES) * wave + 8 * p + lane / 8;
+    aoff[p] = (uint32_t)(std::min(row, rows_here - 1) * HR * DR + ((lane % 8) ^ slot_swz(row)) * 8);
+  }
+#pragma unroll
+  for (int p = 0; p < FB; ++p) {
+    const int row = (NW / WAVES) * wave + 8 * p + lane / 8;
+    boff[p] = (uint32_t)(std::min(row, chunks_here - 1) * HR * DR + ((lane % 8) ^ slot_swz(row)) * 8);
   }
   auto fill = [&](bf16_t *dA, bf16_t *dB, int h, int half) {
     const int o = h * DR + half * SD;
 #pragma unroll
-    for (int p = 0; p < FILLS; ++p) {
-      __builtin_amdgcn_global_load_lds(qt + aoff[p] + o, (lds_void *)(dA + (32 * wave + 8 * p) * SD), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(kt + boff[p] + o, (lds_void *)(dB + (32 * wave + 8 * p) * SD), 16, 0, 0);
-    }
+    for (int p = 0; p < FA; ++p)
+      lds_fill16(qt + aoff[p] + o, dA + ((MW / WAVES) * wave + 8 * p) * SD);
+#pragma unroll
+    for (int p = 0; p < FB; ++p)
+      lds_fill16(kt + boff[p] + o, dB + ((NW / WAVES) * wave + 8 * p) * SD);
   };
   // k-step ks of a stage pairs logical slot 2G + ks of a query row and of a
   // chunk row: lane group G covers the stage's dimensions 16G .. 16G+15
@@ -162,11 +180,11 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
     for (int j = 0; j < 4; ++j) score[i][j] = zero4();
 
   // scales of the tile's rows and chunks (qinv is [h][n_rows], kr_inv_norm [chunk][h])
-  for (int k = tid; k < MW * HR; k += 256) {
+  for (int k = tid; k < MW * HR; k += NT) {
     const int h = k / MW, row = k % MW;
     sqi[h][row] = row < rows_here ? a.qinv[(int64_t)h * n_rows + row0 + row] : 0.f;
   }
-  for (int k = tid; k < NW * HR; k += 256) {
+  for (int k = tid; k < NW * HR; k += NT) {
     const int c = k / HR, h = k % HR;
     sik[h][c] = c < chunks_here ? a.kr_inv_norm[(c0 + c) * HR + h] : 0.f;
   }
@@ -231,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
   for (int q = q_first; q <= q_last; ++q) {
     const int rb_lo = (int)std::max<int64_t>(0, ((int64_t)q * a.t_r - row0) / 16);
     const int rb_hi = (int)std::min<int64_t>(MW / 16, ((int64_t)(q + 1) * a.t_r - row0 + 15) / 16);
-    if (tid < NW) {  // waves 0 and 1, one chunk per lane
+    if (tid < NW) {  // the first NW / 64 waves, one chunk per lane
       float v = -INFINITY;
       for (int i = rb_lo; i < rb_hi; ++i) v = fmaxf(v, red[i][tid]);
       if (a.chunk_out && mydoc >= 0) atomicMax(a.chunk_out + (int64_t)q * a.n_chunks + c0 + tid, score_key(v));
@@ -244,8 +262,8 @@ __global__ __launch_bounds__(256, 2) void route_wide_kernel(RouteArgs a, int n_m
         const int d = __shfl_down(mydoc, o, 64);
         if (lane + o < 64 && d == mydoc) v = fmaxf(v, w);
       }
-      // the first lane of each run in the wave publishes it (a run crossing the
-      // two waves is published by both halves)
+      // the first lane of each run in the wave publishes it (a run crossing
+      // waves is published by each part)
       const int prev = __shfl_up(mydoc, 1, 64);
       if (mydoc >= 0 && (lane == 0 || prev != mydoc))
         atomicMax(a.doc_keys + (int64_t)q * a.n_docs + mydoc, score_key(v));
@@ -270,13 +288,14 @@ hipError_t launch_route_wide(const RouteArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_mtiles = (n_rows + MW - 1) / MW;
-  const int64_t n_ntiles = (a.n_chunks + NW - 1) / NW;
+  const int64_t n_ntiles = (a.n_chunks + WIDE_NW - 1) / WIDE_NW;
   const int64_t grid = 8 * n_mtiles * ((n_ntiles + 7) / 8);
+  const dim3 block(2 * WIDE_NW);
   switch (a.h_r) {
-    case 1: hipLaunchKernelGGL((route_wide_kernel<1, 128>), dim3((unsigned)grid), dim3(256), 0, s, a, n_mtiles, n_ntiles); break;
-    case 2: hipLaunchKernelGGL((route_wide_kernel<2, 128>), dim3((unsigned)grid), dim3(256), 0, s, a, n_mtiles, n_ntiles); break;
-    case 4: hipLaunchKernelGGL((route_wide_kernel<4, 128>), dim3((unsigned)grid), dim3(256), 0, s, a, n_mtiles, n_ntiles); break;
-    case 8: hipLaunchKernelGGL((route_wide_kernel<8, 128>), dim3((unsigned)grid), dim3(256), 0, s, a, n_mtiles, n_ntiles); break;
+    case 1: hipLaunchKernelGGL((route_wide_kernel<1, 128, WIDE_NW>), dim3((unsigned)grid), block, 0, s, a, n_mtiles, n_ntiles); break;
+    case 2: hipLaunchKernelGGL((route_wide_kernel<2, 128, WIDE_NW>), dim3((unsigned)grid), block, 0, s, a, n_mtiles, n_ntiles); break;
+    case 4: hipLaunchKernelGGL((route_wide_kernel<4, 128, WIDE_NW>), dim3((unsigned)grid), block, 0, s, a, n_mtiles, n_ntiles); break;
+    case 8: hipLaunchKernelGGL((route_wide_kernel<8, 128, WIDE_NW>), dim3((unsigned)grid), block, 0, s, a, n_mtiles, n_ntiles); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
