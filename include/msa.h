@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 enum {
   MSA_OK = 0,
@@ -70,11 +70,22 @@ typedef struct msa_rope {
  *   doc_tok_off_host / doc_chunk_off_host: the same arrays in host memory,
  *                 read by msa_pool_memory only (may be NULL elsewhere)
  *   chunk_doc     [n_chunks] int32, owning document of each chunk (written by pool)
- *   kbar, vbar    [h_kv][n_chunks][d]   pooled keys (document-wise RoPE applied) / values
+ *   kbar, vbar    [h_kv][S][d]          pooled keys (document-wise RoPE applied) / values,
+ *                 S = chunk_cap if nonzero, else n_chunks (rows n_chunks..S-1 unused)
  *   krbar         [n_chunks][h_r][d_r]  pooled router keys
  *   kr_inv_norm   [n_chunks][h_r] fp32  1 / ||stored krbar row|| (0 for a zero row)
  * max_doc_len = max L_i and max_doc_chunks = max ceil(L_i/chunk) are host
  * values that msa_bank_layout computes; n_chunks must be below 2^31.
+ *
+ * Incremental append (the pages' corpus updates without re-encoding the
+ * whole memory; [LH] overall architecture, offline encoding once): a bank
+ * allocated with spare capacity -- offset arrays for more documents, chunk
+ * arrays for chunk_cap >= n_chunks chunks -- takes new documents at its end
+ * by extending the offset arrays (device and host), raising n_docs,
+ * n_chunks, max_doc_len and max_doc_chunks, and pooling only the new
+ * document range with msa_pool_memory; pooled rows already in place do not
+ * move.  Re-pooling an existing range replaces it in place (its lengths
+ * must not change).  chunk_cap = 0 means no spare rows.
  */
 typedef struct msa_bank {
   int32_t dtype;
@@ -86,7 +97,7 @@ typedef struct msa_bank {
   int32_t d_r;
   int32_t max_doc_len;
   int32_t max_doc_chunks;
-  int32_t reserved;
+  int32_t chunk_cap;   /* row capacity of kbar/vbar, >= n_chunks; 0 = n_chunks */
   int64_t n_chunks;
   const int64_t *doc_tok_off;
   const int64_t *doc_chunk_off;

@@ -36,12 +36,15 @@ class MsaRope(ctypes.Structure):
 class MsaBank(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("n_docs", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32), ("h_r", ctypes.c_int32), ("d_r", ctypes.c_int32),
-                ("max_doc_len", ctypes.c_int32), ("max_doc_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_doc_len", ctypes.c_int32), ("max_doc_chunks", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
                 ("n_chunks", ctypes.c_int64),
                 ("doc_tok_off", ctypes.c_void_p), ("doc_chunk_off", ctypes.c_void_p),
                 ("doc_tok_off_host", ctypes.c_void_p), ("doc_chunk_off_host", ctypes.c_void_p),
                 ("chunk_doc", ctypes.c_void_p), ("kbar", ctypes.c_void_p), ("vbar", ctypes.c_void_p),
                 ("krbar", ctypes.c_void_p), ("kr_inv_norm", ctypes.c_void_p)]
+
+
+ABI_VERSION = 2  # include/msa.h MSA_ABI_VERSION
 
 
 def _load():
@@ -76,6 +79,8 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    if lib.msa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} implements ABI {lib.msa_abi_version()}, this binding ABI {ABI_VERSION}: rebuild it")
     return lib
 
 

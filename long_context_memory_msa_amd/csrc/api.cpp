@@ -44,6 +44,9 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// row stride of kbar / vbar: the chunk capacity when the bank has spare rows
+int64_t kv_stride(const msa_bank *b) { return b->chunk_cap ? (int64_t)b->chunk_cap : b->n_chunks; }
+
 int check_bank(const msa_bank *b) {
   if (!b) return fail(MSA_ERR_ARG, "bank is null");
   if (b->dtype != MSA_F32 && b->dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "bank dtype %d", b->dtype);
@@ -62,6 +65,8 @@ int check_bank(const msa_bank *b) {
     return fail(MSA_ERR_ARG, "max_doc_chunks = %d != ceil(max_doc_len / chunk)", b->max_doc_chunks);
   if (b->n_chunks > (int64_t)b->n_docs * b->max_doc_chunks)
     return fail(MSA_ERR_ARG, "n_chunks exceeds n_docs * max_doc_chunks");
+  if (b->chunk_cap != 0 && b->chunk_cap < b->n_chunks)
+    return fail(MSA_ERR_ARG, "chunk_cap = %d below n_chunks = %lld", b->chunk_cap, (long long)b->n_chunks);
   CHECK_PTR(b->doc_tok_off, 8, "bank.doc_tok_off");
   CHECK_PTR(b->doc_chunk_off, 8, "bank.doc_chunk_off");
   CHECK_PTR(b->chunk_doc, 4, "bank.chunk_doc");
@@ -110,6 +115,7 @@ msa::AttendArgs attend_args(const msa_bank *b, const void *Q, const void *K_loc,
   a.d = b->d;
   a.h_q = h_q;
   a.n_chunks = b->n_chunks;
+  a.kv_stride = kv_stride(b);
   a.n_docs = b->n_docs;
   a.doc_chunk_off = b->doc_chunk_off;
   a.kbar = b->kbar;
@@ -271,6 +277,7 @@ int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void 
     a.d_r = b->d_r;
     a.chunk = b->chunk;
     a.n_chunks = b->n_chunks;
+    a.kv_stride = kv_stride(b);
     a.doc_begin = doc_begin;
     a.doc_end = doc_end;
     a.slab_tok0 = to[doc_begin];

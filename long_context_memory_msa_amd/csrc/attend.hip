@@ -168,8 +168,8 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb) acc_o[mb] = zero4();
 
-  const T *kbar = static_cast<const T *>(a.kbar) + (int64_t)kvh * a.n_chunks * D;
-  const T *vbar = static_cast<const T *>(a.vbar) + (int64_t)kvh * a.n_chunks * D;
+  const T *kbar = static_cast<const T *>(a.kbar) + (int64_t)kvh * a.kv_stride * D;
+  const T *vbar = static_cast<const T *>(a.vbar) + (int64_t)kvh * a.kv_stride * D;
   const T *kloc = static_cast<const T *>(a.K_loc);
   const T *vloc = static_cast<const T *>(a.V_loc);
 

@@ -15,7 +15,8 @@ hipError_t launch_rope_table(float *cos, float *sin, int max_pos, int d, double 
 struct PoolArgs {
   int dtype;                     // 0 fp32, 1 bf16
   int h_kv, d, h_r, d_r, chunk;
-  int64_t n_chunks;              // bank chunks (row stride of kbar / vbar)
+  int64_t n_chunks;              // bank chunks
+  int64_t kv_stride;             // row stride of kbar / vbar (chunk capacity)
   int doc_begin, doc_end;        // slab documents
   int64_t slab_tok0;             // first token of doc_begin
   int64_t chunk_begin, chunk_end;
@@ -108,6 +109,7 @@ struct AttendArgs {
   int dtype;
   int h_kv, d, h_q;
   int64_t n_chunks;
+  int64_t kv_stride;  // row stride of kbar / vbar (chunk capacity)
   int n_docs;
   const int64_t *doc_chunk_off;
   const void *kbar, *vbar;

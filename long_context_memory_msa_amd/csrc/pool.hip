@@ -133,12 +133,12 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     if (u < a.h_kv) {  // K head u: document-wise RoPE at in-document positions
       const T *src = static_cast<const T *>(a.K) + row0 * (a.h_kv * D) + u * D;
       row_sum<T, D, true>(src, a.h_kv * D, n_tok, (int)j0, a.cos, a.sin, acc, lane);
-      store_row<T, D>(static_cast<T *>(a.kbar) + ((int64_t)u * a.n_chunks + c) * D, acc, n_tok, lane, nullptr);
+      store_row<T, D>(static_cast<T *>(a.kbar) + ((int64_t)u * a.kv_stride + c) * D, acc, n_tok, lane, nullptr);
     } else if (u < 2 * a.h_kv) {
       const int h = u - a.h_kv;
       const T *src = static_cast<const T *>(a.V) + row0 * (a.h_kv * D) + h * D;
       row_sum<T, D, false>(src, a.h_kv * D, n_tok, 0, nullptr, nullptr, acc, lane);
-      store_row<T, D>(static_cast<T *>(a.vbar) + ((int64_t)h * a.n_chunks + c) * D, acc, n_tok, lane, nullptr);
+      store_row<T, D>(static_cast<T *>(a.vbar) + ((int64_t)h * a.kv_stride + c) * D, acc, n_tok, lane, nullptr);
     } else {
       const int h = u - 2 * a.h_kv;
       const T *src = static_cast<const T *>(a.KR) + row0 * (a.h_r * DR) + h * DR;

@@ -29,30 +29,73 @@ class Rope:
 
 
 class Bank:
-    """Pooled memory bank of one routed layer, resident in HBM."""
+    """Pooled memory bank of one routed layer, resident in HBM.
+
+    ``cap_docs`` / ``cap_chunks`` reserve room for documents appended later
+    (``append``): the offset arrays hold cap_docs + 1 entries and the chunk
+    arrays cap_chunks rows, so new documents are pooled in place without
+    moving the ones already encoded.
+    """
 
     def __init__(self, doc_lens: Sequence[int], chunk: int, h_kv: int, d: int, h_r: int, d_r: int, dtype: str,
-                 device="cuda"):
+                 device="cuda", cap_docs: Optional[int] = None, cap_chunks: Optional[int] = None):
         lay = _lib.msa_bank_layout(doc_lens, chunk)
         self.dtype = dtype
+        self.chunk = chunk
         self.layout = lay
         self.n_docs = len(doc_lens)
         self.n_chunks = lay["n_chunks"]
+        cap_docs = self.n_docs if cap_docs is None else int(cap_docs)
+        cap_chunks = self.n_chunks if cap_chunks is None else int(cap_chunks)
+        if cap_docs < self.n_docs or cap_chunks < self.n_chunks:
+            raise ValueError("capacity below the initial documents")
+        self.cap_docs, self.cap_chunks = cap_docs, cap_chunks
         td = TORCH_DTYPE[dtype]
-        self.doc_tok_off_host = np.ascontiguousarray(lay["doc_tok_off"])
-        self.doc_chunk_off_host = np.ascontiguousarray(lay["doc_chunk_off"])
+        self.doc_tok_off_host = np.zeros(cap_docs + 1, dtype=np.int64)
+        self.doc_chunk_off_host = np.zeros(cap_docs + 1, dtype=np.int64)
+        self.doc_tok_off_host[:self.n_docs + 1] = lay["doc_tok_off"]
+        self.doc_chunk_off_host[:self.n_docs + 1] = lay["doc_chunk_off"]
         self.doc_tok_off = torch.from_numpy(self.doc_tok_off_host).to(device)
         self.doc_chunk_off = torch.from_numpy(self.doc_chunk_off_host).to(device)
-        self.chunk_doc = torch.empty(self.n_chunks, dtype=torch.int32, device=device)
-        self.kbar = torch.empty((h_kv, self.n_chunks, d), dtype=td, device=device)
-        self.vbar = torch.empty((h_kv, self.n_chunks, d), dtype=td, device=device)
-        self.krbar = torch.empty((self.n_chunks, h_r, d_r), dtype=td, device=device)
-        self.kr_inv_norm = torch.empty((self.n_chunks, h_r), dtype=torch.float32, device=device)
+        self.chunk_doc = torch.empty(cap_chunks, dtype=torch.int32, device=device)
+        self.kbar = torch.empty((h_kv, cap_chunks, d), dtype=td, device=device)
+        self.vbar = torch.empty((h_kv, cap_chunks, d), dtype=td, device=device)
+        self.krbar = torch.empty((cap_chunks, h_r, d_r), dtype=td, device=device)
+        self.kr_inv_norm = torch.empty((cap_chunks, h_r), dtype=torch.float32, device=device)
         self.c = _lib.MsaBank(
-            ABI_DTYPE[dtype], self.n_docs, chunk, h_kv, d, h_r, d_r, lay["max_doc_len"], lay["max_doc_chunks"], 0,
-            self.n_chunks, self.doc_tok_off.data_ptr(), self.doc_chunk_off.data_ptr(),
+            ABI_DTYPE[dtype], self.n_docs, chunk, h_kv, d, h_r, d_r, lay["max_doc_len"], lay["max_doc_chunks"],
+            cap_chunks, self.n_chunks, self.doc_tok_off.data_ptr(), self.doc_chunk_off.data_ptr(),
             self.doc_tok_off_host.ctypes.data, self.doc_chunk_off_host.ctypes.data, self.chunk_doc.data_ptr(),
             self.kbar.data_ptr(), self.vbar.data_ptr(), self.krbar.data_ptr(), self.kr_inv_norm.data_ptr())
+
+    def append(self, doc_lens: Sequence[int]) -> tuple:
+        """Add documents at the end of the bank (offsets and counts only);
+        returns their range (doc_begin, doc_end) for ``pool``.  Nothing is
+        enqueued on the device except the copy of the new offsets."""
+        lens = np.asarray(doc_lens, dtype=np.int64)
+        if lens.size == 0:
+            return self.n_docs, self.n_docs
+        if (lens < 1).any():
+            raise ValueError("document lengths must be >= 1")
+        n0, c0 = self.n_docs, self.n_chunks
+        nch = (lens + self.chunk - 1) // self.chunk
+        n1, c1 = n0 + lens.size, c0 + int(nch.sum())
+        if n1 > self.cap_docs or c1 > self.cap_chunks:
+            raise ValueError(f"bank capacity exceeded: {n1} documents / {c1} chunks "
+                             f"(capacity {self.cap_docs} / {self.cap_chunks})")
+        self.doc_tok_off_host[n0 + 1:n1 + 1] = self.doc_tok_off_host[n0] + np.cumsum(lens)
+        self.doc_chunk_off_host[n0 + 1:n1 + 1] = c0 + np.cumsum(nch)
+        self.doc_tok_off[n0 + 1:n1 + 1].copy_(torch.from_numpy(self.doc_tok_off_host[n0 + 1:n1 + 1]))
+        self.doc_chunk_off[n0 + 1:n1 + 1].copy_(torch.from_numpy(self.doc_chunk_off_host[n0 + 1:n1 + 1]))
+        self.n_docs, self.n_chunks = n1, c1
+        self.c.n_docs, self.c.n_chunks = n1, c1
+        self.c.max_doc_len = max(int(self.c.max_doc_len), int(lens.max()))
+        self.c.max_doc_chunks = (self.c.max_doc_len + self.chunk - 1) // self.chunk
+        return n0, n1
+
+    @property
+    def doc_lens(self) -> np.ndarray:
+        return np.diff(self.doc_tok_off_host[:self.n_docs + 1])
 
     def pool(self, K, V, KR, doc_begin: int, doc_end: int, rope: Rope, stream=None) -> None:
         """Offline pooling of documents [doc_begin, doc_end) from a token slab."""

@@ -34,11 +34,16 @@ def slab_ranges(doc_tok_off: np.ndarray, slab_tokens: int) -> List[tuple]:
 
 
 def encode_bank(bank: Bank, rope: Rope, fill: Callable, slab_tokens: int, h_kv: int, d: int, h_r: int, d_r: int,
-                time_slabs: bool = False) -> dict:
-    """Pool the whole bank slab by slab; returns slab count and (optionally)
-    the pooling kernels' time and raw bytes read per slab."""
-    off = bank.doc_tok_off_host
-    ranges = slab_ranges(off, slab_tokens)
+                time_slabs: bool = False, docs: tuple = None) -> dict:
+    """Pool the bank's documents slab by slab -- all of them, or the range
+    ``docs`` = (doc_begin, doc_end), e.g. the documents just appended; returns
+    the slab count and (optionally) the pooling kernels' time and raw bytes
+    read per slab."""
+    off = bank.doc_tok_off_host[:bank.n_docs + 1]
+    lo, hi = (0, bank.n_docs) if docs is None else docs
+    ranges = [(a + lo, b + lo) for a, b in slab_ranges(off[lo:hi + 1] - off[lo], slab_tokens)] if hi > lo else []
+    if not ranges:
+        return {"slabs": 0, "seconds": [], "raw_bytes": []}
     cap = max(int(off[b] - off[a]) for a, b in ranges)
     td = TORCH_DTYPE[bank.dtype]
     dev = bank.kbar.device

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_empty_error():
-    assert msa.msa_abi_version() == 1
+    assert msa.msa_abi_version() == 2
     msa.msa_bank_layout([3], 2)
     assert msa.msa_last_error() == ""
 
@@ -95,8 +95,31 @@ def test_bank_validation():
     for over, code in (({"dtype": 7}, L.MSA_ERR_UNSUPPORTED), ({"d": 96}, L.MSA_ERR_UNSUPPORTED),
                        ({"h_r": 3}, L.MSA_ERR_UNSUPPORTED), ({"n_docs": 0}, L.MSA_ERR_ARG),
                        ({"max_doc_chunks": 9}, L.MSA_ERR_ARG), ({"kbar": None}, L.MSA_ERR_ARG),
-                       ({"krbar": MIS.addr}, L.MSA_ERR_ARG), ({"n_chunks": 1}, L.MSA_ERR_ARG)):
+                       ({"krbar": MIS.addr}, L.MSA_ERR_ARG), ({"n_chunks": 1}, L.MSA_ERR_ARG),
+                       ({"chunk_cap": 15}, L.MSA_ERR_ARG), ({"chunk_cap": -1}, L.MSA_ERR_ARG)):
         assert _code(msa.msa_route_score, _bank(**over), A, 1, 1, A, None, A, 1 << 30, stream=0) == code, over
+
+
+def test_bank_capacity_host_side():
+    # a bank with room for later documents: offsets and counts grow, capacity fixed
+    import torch
+    lens = [300, 129, 1]
+    from long_context_memory_msa_amd.memory import Bank
+    b = Bank(lens, 128, 2, 64, 2, 64, "f32", device="cpu", cap_docs=6, cap_chunks=12)
+    assert (b.n_docs, b.n_chunks, b.c.chunk_cap) == (3, 6, 12)
+    assert tuple(b.kbar.shape) == (2, 12, 64) and tuple(b.krbar.shape) == (12, 2, 64)
+    assert b.append([128, 500]) == (3, 5)
+    assert (b.n_docs, b.n_chunks, b.c.n_docs, b.c.n_chunks) == (5, 11, 5, 11)
+    assert b.doc_lens.tolist() == [300, 129, 1, 128, 500]
+    assert b.doc_chunk_off_host[:6].tolist() == [0, 3, 5, 6, 7, 11]
+    assert b.doc_tok_off.tolist()[:6] == [0, 300, 429, 430, 558, 1058]
+    assert (b.c.max_doc_len, b.c.max_doc_chunks) == (500, 4)
+    assert b.append([]) == (5, 5)
+    with pytest.raises(ValueError):
+        b.append([129])          # 2 more chunks > capacity 12
+    with pytest.raises(ValueError):
+        b.append([0])
+    assert isinstance(b.kbar, torch.Tensor)
 
 
 def test_route_validation():

@@ -276,6 +276,49 @@ def test_layer_end_to_end(device, name):
         assert_attention_close(host(out), want["O"])
 
 
+def test_bank_append_equals_one_pass_encoding(device):
+    # incremental update: half the documents encoded into a bank with spare
+    # capacity, routed (checked against the oracle on that half), then the
+    # rest appended and pooled in place -- the result equals the bank encoded
+    # in one pass, value for value, and so does the layer over it
+    cfg, bt = SMALL["cfg2"]
+    w = _wl(cfg, bt)
+    qi, K, V, KR = host_inputs(w)
+    full, rope = gpu_bank_pooled(w, K, V, KR, device, 2)
+    half = w.n_docs // 2
+    t1 = int(w.doc_tok_off[half])
+    log(f"append: {half} + {w.n_docs - half} docs, {w.n_chunks} chunks")
+    bank = M.Bank(w.doc_lens[:half], w.chunk, w.h_kv, w.d, w.h_r, w.d_r, w.dtype, device,
+                  cap_docs=w.n_docs + 3, cap_chunks=w.n_chunks + 50)
+    bank.pool(dev(K[:t1], w.dtype, device), dev(V[:t1], w.dtype, device), dev(KR[:t1], w.dtype, device), 0, half,
+              rope)
+    wh = dataclasses.replace(w, doc_lens=w.doc_lens[:half], gold=np.zeros((w.n_q, 0), np.int64))
+    QR, Q, Kl, Vl = query_views(w, qi, device)
+    _, _, _, s_half = run_layer(bank, rope, wh, QR, Q, Kl, Vl, device)
+    obh = O.pool(wh.doc_lens, w.chunk, K[:t1], V[:t1], KR[:t1], w.dtype, w.rope_base)
+    S = O.chunk_scores(qi["QR"][:, w.L_loc - w.T_route:w.L_loc], obh["krbar"])
+    assert np.abs(host(s_half) - O.doc_scores(S, obh["doc_chunk_off"])).max() <= 2e-3
+    a, b = bank.append(w.doc_lens[half:])
+    assert (a, b) == (half, w.n_docs) and bank.n_chunks == w.n_chunks
+    bank.pool(dev(K[t1:], w.dtype, device), dev(V[t1:], w.dtype, device), dev(KR[t1:], w.dtype, device), a, b, rope)
+    torch.cuda.synchronize()
+    n = w.n_chunks
+    assert torch.equal(bank.kbar[:, :n], full.kbar) and torch.equal(bank.vbar[:, :n], full.vbar)
+    assert torch.equal(bank.krbar[:n], full.krbar) and torch.equal(bank.kr_inv_norm[:n], full.kr_inv_norm)
+    assert torch.equal(bank.chunk_doc[:n], full.chunk_doc)
+    assert torch.equal(bank.doc_chunk_off[:w.n_docs + 1], full.doc_chunk_off)
+    got = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+    ref = run_layer(full, rope, w, QR, Q, Kl, Vl, device)
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
+    # re-pooling an existing range in place leaves it unchanged
+    t0, t2 = int(w.doc_tok_off[2]), int(w.doc_tok_off[5])
+    bank.pool(dev(K[t0:t2], w.dtype, device), dev(V[t0:t2], w.dtype, device), dev(KR[t0:t2], w.dtype, device), 2, 5,
+              rope)
+    torch.cuda.synchronize()
+    assert torch.equal(bank.kbar[:, :n], full.kbar) and torch.equal(bank.krbar[:n], full.krbar)
+
+
 def test_layer_equals_composition_and_is_deterministic(device):
     w = _wl(3, 300_000)
     qi, K, V, KR = host_inputs(w)
