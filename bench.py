@@ -209,6 +209,98 @@ def bench_interleave(args) -> int:
     return 0
 
 
+def bench_tiered(args) -> int:
+    """The 100M-token decode layer with a tiered bank: pooled keys/values in
+    pinned host memory (read by the attention over the host link), router keys
+    in HBM.  Steps of the same query batch run through the two-stream pipeline
+    (attention of step s during the routing of step s+1); one sequential step
+    with stage events gives the breakdown."""
+    import numpy as np
+    import torch
+
+    from synth import device as sdev, workloads as W
+    from long_context_memory_msa_amd import _lib as L, memory as M, offline
+    from long_context_memory_msa_amd.pipeline import DecodePipeline
+
+    dev = torch.device("cuda:0")
+    w = W.make_workload(3, bank_tokens=args.bank_tokens)
+    print(f"[bench] tiered {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr,
+          flush=True)
+    qi = W.query_inputs(w)
+    uhat = torch.from_numpy(W.gold_uhat(w, qi["QR"])).to(dev)
+    td = M.TORCH_DTYPE[w.dtype]
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(td).contiguous()
+
+    QR = up(qi["QR"][:, w.L_loc - w.T_route:w.L_loc])
+    Q = up(qi["Q"][:, w.L_loc - w.T:w.L_loc])
+    Kl = up(qi["K_loc"][:, :w.L_loc])
+    Vl = up(qi["V_loc"][:, :w.L_loc])
+    bank = M.Bank(w.doc_lens, w.chunk, w.h_kv, w.d, w.h_r, w.d_r, w.dtype, dev, kv_host=True)
+    rope = M.Rope(w.max_pos, w.d, w.rope_base, dev)
+    t0 = time.perf_counter()
+    offline.encode_bank(bank, rope, lambda a, b, K, V, KR: sdev.fill_raw_slab(w, 0, a, b, K, V, KR, uhat),
+                        args.slab_tokens, w.h_kv, w.d, w.h_r, w.d_r)
+    print(f"[bench] tiered bank encoded in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    scale = L.default_scale(w.d)
+
+    # sequential steps (one stream, stage events)
+    O_ = torch.empty((w.n_q, w.T, w.h_q, w.d), dtype=td, device=dev)
+    idx = torch.empty((w.n_q, w.k), dtype=torch.int32, device=dev)
+    val = torch.empty((w.n_q, w.k), dtype=torch.float32, device=dev)
+    nb = L.msa_layer_workspace_bytes(bank.c, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k)
+    ws = M.workspace(nb, dev)
+    n_seq = 10
+    for _ in range(3):
+        L.msa_layer_forward(bank.c, Q, Kl, Vl, QR, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, scale,
+                            rope.c, O_, idx, val, None, ws, nb)
+    torch.cuda.synchronize()
+    ev = Events(4 * n_seq)
+    for i in range(n_seq):
+        L.msa_layer_forward(bank.c, Q, Kl, Vl, QR, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, scale,
+                            rope.c, O_, idx, val, None, ws, nb, ev.h[4 * i:4 * i + 4])
+    torch.cuda.synchronize()
+    st = {name: statistics.median(ev.ms(ev.h[4 * i + a], ev.h[4 * i + b]) for i in range(n_seq))
+          for name, a, b in (("route", 0, 1), ("topk", 1, 2), ("attend", 2, 3), ("layer", 0, 3))}
+    ev.close()
+    off = w.doc_chunk_off
+    gi = idx.cpu().numpy()
+    n_sel = sum(int(off[d + 1] - off[d]) for q in range(w.n_q) for d in gi[q])
+    gathered = n_sel * w.h_kv * w.d * 2 * 2   # K and V rows of the selected chunks, bf16
+
+    # pipelined steps
+    pipe = DecodePipeline(bank, rope, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, scale, dev)
+    for _ in range(args.warmup):
+        pipe.step(QR, Q, Kl, Vl)
+    pipe.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pipe.step(QR, Q, Kl, Vl)
+    pipe.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    rec = {
+        "metric": "memory tokens routed/sec, tiered bank (Kbar/Vbar in pinned host memory), pipelined decode",
+        "value": w.n_tok / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "100M-token bank, decode 16 queries x 1 token, k=16; Kbar/Vbar in host memory",
+                   "n_chunks": w.n_chunks},
+        "sequential_stage_ms": st,
+        "attend_gather": {"bytes": gathered, "GB/s": gathered / (st["attend"] * 1e-3) / 1e9},
+        "hbm_bytes": bank.bytes_resident(),
+        "host_bytes": bank.kbar.numel() * bank.kbar.element_size() * 2,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,9 +310,10 @@ def main() -> int:
                     help="oracle baseline sample: first N documents (-1 = the whole bank, 0 = skip)")
     ap.add_argument("--bank-tokens", type=int, default=None, help="smaller bank for a quick look (not the metric)")
     ap.add_argument("--slab-tokens", type=int, default=8_000_000)
-    ap.add_argument("--workload", choices=["decode100m", "interleave"], default="decode100m",
+    ap.add_argument("--workload", choices=["decode100m", "interleave", "tiered"], default="decode100m",
                     help="decode100m: the headline layer (default); interleave: 18 routed layers x 10M tokens, "
-                         "3 Memory Interleave rounds (MFMA-bound prefill report)")
+                         "3 Memory Interleave rounds (MFMA-bound prefill report); tiered: the decode layer with "
+                         "Kbar/Vbar in host memory, two-stream pipeline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -250,6 +343,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.workload == "interleave":
         return bench_interleave(args)
+    if args.workload == "tiered":
+        return bench_tiered(args)
     w = W.make_workload(3, bank_tokens=args.bank_tokens)
     print(f"[bench] {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr, flush=True)
 

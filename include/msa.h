@@ -77,6 +77,16 @@ typedef struct msa_rope {
  * max_doc_len = max L_i and max_doc_chunks = max ceil(L_i/chunk) are host
  * values that msa_bank_layout computes; n_chunks must be below 2^31.
  *
+ * Tiered bank (the pages' deployment keeps Kbar/Vbar in host memory and only
+ * the router keys on the GPU; [HD] key engineering details; [WC] mechanism
+ * 3): kbar and vbar may live in pinned host memory mapped into the device
+ * address space (their device addresses from msa_device_pointer; set
+ * kv_host).  Pooling then writes them over the host link and sparse
+ * attention gathers the selected documents' rows from there, with few
+ * workgroups (the host link, not the GPU, bounds the gather, and the rest of
+ * the GPU stays free for a concurrent router scan); the scan reads only
+ * krbar, kr_inv_norm and chunk_doc, which stay in HBM.
+ *
  * Incremental append (the pages' corpus updates without re-encoding the
  * whole memory; [LH] overall architecture, offline encoding once): a bank
  * allocated with spare capacity -- offset arrays for more documents, chunk
@@ -98,6 +108,8 @@ typedef struct msa_bank {
   int32_t max_doc_len;
   int32_t max_doc_chunks;
   int32_t chunk_cap;   /* row capacity of kbar/vbar, >= n_chunks; 0 = n_chunks */
+  int32_t kv_host;     /* nonzero: kbar/vbar in pinned host memory (tiered bank) */
+  int32_t reserved;    /* 0 */
   int64_t n_chunks;
   const int64_t *doc_tok_off;
   const int64_t *doc_chunk_off;
@@ -115,6 +127,15 @@ int msa_abi_version(void);
 
 /* Message of the last failed call on this thread ("" after success). */
 const char *msa_last_error(void);
+
+/*
+ * Device address of pinned, device-mapped host memory (as allocated by
+ * hipHostMalloc), for the kbar / vbar pointers of a tiered bank.
+ * host: host pointer into such an allocation; *dev receives the address
+ * kernels use (host memory).  Errors: MSA_ERR_ARG on null pointers or when
+ * the runtime does not know `host` as pinned device-mapped memory.
+ */
+int msa_device_pointer(const void *host, void **dev);
 
 /*
  * Host helper: bank layout from document lengths (all pointers host).

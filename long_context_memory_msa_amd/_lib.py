@@ -37,6 +37,7 @@ class MsaBank(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("n_docs", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32), ("h_r", ctypes.c_int32), ("d_r", ctypes.c_int32),
                 ("max_doc_len", ctypes.c_int32), ("max_doc_chunks", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
+                ("kv_host", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("n_chunks", ctypes.c_int64),
                 ("doc_tok_off", ctypes.c_void_p), ("doc_chunk_off", ctypes.c_void_p),
                 ("doc_tok_off_host", ctypes.c_void_p), ("doc_chunk_off_host", ctypes.c_void_p),
@@ -61,6 +62,7 @@ def _load():
     sig = {
         "msa_abi_version": ([], ctypes.c_int),
         "msa_last_error": ([], ctypes.c_char_p),
+        "msa_device_pointer": ([P, P], ctypes.c_int),
         "msa_bank_layout": ([P, I32, I32, P, P, P, P, P], ctypes.c_int),
         "msa_rope_table": ([P, P, I32, I32, D, P], ctypes.c_int),
         "msa_pool_memory": ([bank_p, P, P, P, I32, I32, rope_p, P], ctypes.c_int),
@@ -110,6 +112,14 @@ def _check(rc: int) -> None:
 # ---------------------------------------------------------------------------
 def msa_abi_version() -> int:
     return _lib.msa_abi_version()
+
+
+def msa_device_pointer(host_ptr: int) -> int:
+    """Device address of pinned, device-mapped host memory (a torch tensor made
+    with pin_memory=True is one)."""
+    out = ctypes.c_void_p()
+    _check(_lib.msa_device_pointer(ctypes.c_void_p(host_ptr), ctypes.byref(out)))
+    return int(out.value)
 
 
 def msa_last_error() -> str:

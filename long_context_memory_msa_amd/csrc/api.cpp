@@ -116,6 +116,7 @@ msa::AttendArgs attend_args(const msa_bank *b, const void *Q, const void *K_loc,
   a.h_q = h_q;
   a.n_chunks = b->n_chunks;
   a.kv_stride = kv_stride(b);
+  a.kv_host = b->kv_host != 0;
   a.n_docs = b->n_docs;
   a.doc_chunk_off = b->doc_chunk_off;
   a.kbar = b->kbar;
@@ -203,6 +204,18 @@ extern "C" {
 int msa_abi_version(void) { return MSA_ABI_VERSION; }
 
 const char *msa_last_error(void) { return g_err.c_str(); }
+
+int msa_device_pointer(const void *host, void **dev) {
+  if (!host || !dev) return fail(MSA_ERR_ARG, "null pointer");
+  void *d = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&d, const_cast<void *>(host), 0);
+  if (e != hipSuccess || !d) {
+    (void)hipGetLastError();  // clear the runtime's sticky error for the caller's next call
+    return fail(MSA_ERR_ARG, "not pinned device-mapped host memory (%s)", hipGetErrorString(e));
+  }
+  *dev = d;
+  return ok();
+}
 
 int msa_bank_layout(const int64_t *doc_lens, int32_t n_docs, int32_t chunk, int64_t *doc_tok_off,
                     int64_t *doc_chunk_off, int64_t *n_chunks, int32_t *max_doc_len, int32_t *max_doc_chunks) {

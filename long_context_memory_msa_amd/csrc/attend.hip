@@ -425,7 +425,10 @@ Plan plan(const AttendArgs &a) {
   const int64_t base = (int64_t)a.n_q * a.h_kv * p.n_rbg;
   const int64_t est_keys = std::min<int64_t>((int64_t)a.k * std::max(1, a.max_doc_chunks), a.n_chunks) + a.L_loc;
   const int64_t tiles = (est_keys + KT - 1) / KT;
-  int64_t ns = ((int64_t)MSA_ATTEND_SPLIT_MUL * device_cu_count() + base - 1) / base;
+  // keys/values in host memory: the host link bounds the gather, and a
+  // workgroup per (query, KV head, row group) keeps enough rows in flight
+  // while leaving the GPU to a concurrent router scan
+  int64_t ns = a.kv_host ? 1 : ((int64_t)MSA_ATTEND_SPLIT_MUL * device_cu_count() + base - 1) / base;
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / MSA_ATTEND_MIN_TILES));
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, 64));
   p.n_split = (int)ns;

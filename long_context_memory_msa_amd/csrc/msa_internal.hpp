@@ -110,6 +110,7 @@ struct AttendArgs {
   int h_kv, d, h_q;
   int64_t n_chunks;
   int64_t kv_stride;  // row stride of kbar / vbar (chunk capacity)
+  int kv_host;        // kbar / vbar in host memory: gather with few workgroups
   int n_docs;
   const int64_t *doc_chunk_off;
   const void *kbar, *vbar;

@@ -35,10 +35,15 @@ class Bank:
     (``append``): the offset arrays hold cap_docs + 1 entries and the chunk
     arrays cap_chunks rows, so new documents are pooled in place without
     moving the ones already encoded.
+
+    ``kv_host=True`` makes a tiered bank: the pooled keys/values (two thirds
+    of the bytes) live in pinned host memory that the GPU reads directly,
+    only the router keys, their norms and the layout stay in HBM.
     """
 
     def __init__(self, doc_lens: Sequence[int], chunk: int, h_kv: int, d: int, h_r: int, d_r: int, dtype: str,
-                 device="cuda", cap_docs: Optional[int] = None, cap_chunks: Optional[int] = None):
+                 device="cuda", cap_docs: Optional[int] = None, cap_chunks: Optional[int] = None,
+                 kv_host: bool = False):
         lay = _lib.msa_bank_layout(doc_lens, chunk)
         self.dtype = dtype
         self.chunk = chunk
@@ -58,15 +63,22 @@ class Bank:
         self.doc_tok_off = torch.from_numpy(self.doc_tok_off_host).to(device)
         self.doc_chunk_off = torch.from_numpy(self.doc_chunk_off_host).to(device)
         self.chunk_doc = torch.empty(cap_chunks, dtype=torch.int32, device=device)
-        self.kbar = torch.empty((h_kv, cap_chunks, d), dtype=td, device=device)
-        self.vbar = torch.empty((h_kv, cap_chunks, d), dtype=td, device=device)
+        self.kv_host = kv_host
+        if kv_host:
+            self.kbar = torch.empty((h_kv, cap_chunks, d), dtype=td, pin_memory=True)
+            self.vbar = torch.empty((h_kv, cap_chunks, d), dtype=td, pin_memory=True)
+            kv_ptr = (_lib.msa_device_pointer(self.kbar.data_ptr()), _lib.msa_device_pointer(self.vbar.data_ptr()))
+        else:
+            self.kbar = torch.empty((h_kv, cap_chunks, d), dtype=td, device=device)
+            self.vbar = torch.empty((h_kv, cap_chunks, d), dtype=td, device=device)
+            kv_ptr = (self.kbar.data_ptr(), self.vbar.data_ptr())
         self.krbar = torch.empty((cap_chunks, h_r, d_r), dtype=td, device=device)
         self.kr_inv_norm = torch.empty((cap_chunks, h_r), dtype=torch.float32, device=device)
         self.c = _lib.MsaBank(
             ABI_DTYPE[dtype], self.n_docs, chunk, h_kv, d, h_r, d_r, lay["max_doc_len"], lay["max_doc_chunks"],
-            cap_chunks, self.n_chunks, self.doc_tok_off.data_ptr(), self.doc_chunk_off.data_ptr(),
+            cap_chunks, int(kv_host), 0, self.n_chunks, self.doc_tok_off.data_ptr(), self.doc_chunk_off.data_ptr(),
             self.doc_tok_off_host.ctypes.data, self.doc_chunk_off_host.ctypes.data, self.chunk_doc.data_ptr(),
-            self.kbar.data_ptr(), self.vbar.data_ptr(), self.krbar.data_ptr(), self.kr_inv_norm.data_ptr())
+            kv_ptr[0], kv_ptr[1], self.krbar.data_ptr(), self.kr_inv_norm.data_ptr())
 
     def append(self, doc_lens: Sequence[int]) -> tuple:
         """Add documents at the end of the bank (offsets and counts only);
@@ -102,9 +114,11 @@ class Bank:
         _lib.msa_pool_memory(self.c, K, V, KR, doc_begin, doc_end, rope.c, stream)
 
     def bytes_resident(self) -> int:
-        return sum(t.numel() * t.element_size() for t in
-                   (self.kbar, self.vbar, self.krbar, self.kr_inv_norm, self.chunk_doc, self.doc_tok_off,
-                    self.doc_chunk_off))
+        """Bytes of the bank in HBM (the host tier not counted)."""
+        ts = [self.krbar, self.kr_inv_norm, self.chunk_doc, self.doc_tok_off, self.doc_chunk_off]
+        if not self.kv_host:
+            ts += [self.kbar, self.vbar]
+        return sum(t.numel() * t.element_size() for t in ts)
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

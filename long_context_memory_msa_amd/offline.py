@@ -46,7 +46,7 @@ def encode_bank(bank: Bank, rope: Rope, fill: Callable, slab_tokens: int, h_kv: 
         return {"slabs": 0, "seconds": [], "raw_bytes": []}
     cap = max(int(off[b] - off[a]) for a, b in ranges)
     td = TORCH_DTYPE[bank.dtype]
-    dev = bank.kbar.device
+    dev = bank.krbar.device
     K = torch.empty((cap, h_kv, d), dtype=td, device=dev)
     V = torch.empty((cap, h_kv, d), dtype=td, device=dev)
     KR = torch.empty((cap, h_r, d_r), dtype=td, device=dev)

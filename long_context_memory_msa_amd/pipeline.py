@@ -1,0 +1,75 @@
+"""Decode steps of independent query batches with the attention of one step
+overlapping the routing of the next.
+
+The pages keep the pooled keys/values in host memory and load the selected
+documents' rows asynchronously, overlapped with the search (hotdry blog, key
+engineering details: tiered storage and asynchronous prefetch; wiselychen
+blog, mechanism 3).  With a tiered bank (``Bank(kv_host=True)``) the
+attention gathers those rows over the host link, a different resource from
+the HBM stream of the router scan, so the two can run at once on two streams:
+
+  route stream:  [wait attend(s-2) done] route_score(s) -> topk(s) -> mark selected(s)
+  attend stream: [wait selected(s)] sparse_attend(s) -> mark done(s)
+
+Outputs are double-buffered by step parity: step s writes slot s % 2, which
+stays valid until step s + 2 is issued.  All computation runs in the library's
+kernels; this module only orders launches on streams.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from .memory import TORCH_DTYPE, Bank, Rope, workspace
+
+
+class DecodePipeline:
+    def __init__(self, bank: Bank, rope: Rope, n_q: int, T: int, t_r: int, L_loc: int, h_q: int, k: int, pos0: int,
+                 scale: Optional[float] = None, device="cuda"):
+        self.bank, self.rope = bank, rope
+        self.n_q, self.T, self.t_r, self.L_loc, self.h_q, self.k, self.pos0 = n_q, T, t_r, L_loc, h_q, k, pos0
+        d = bank.c.d
+        self.scale = _lib.default_scale(d) if scale is None else scale
+        c = bank.c
+        self.ws_route_n = _lib.msa_route_workspace_bytes(c, n_q, t_r)
+        self.ws_topk_n = _lib.msa_topk_workspace_bytes(n_q, c.n_docs, k)
+        self.ws_attend_n = _lib.msa_attend_workspace_bytes(c, n_q, T, L_loc, h_q, k)
+        self.ws_route = workspace(self.ws_route_n, device)
+        self.ws_topk = workspace(self.ws_topk_n, device)
+        self.ws_attend = workspace(self.ws_attend_n, device)
+        td = TORCH_DTYPE[bank.dtype]
+        self.s_doc = [torch.empty((n_q, c.n_docs), dtype=torch.float32, device=device) for _ in range(2)]
+        self.idx = [torch.empty((n_q, k), dtype=torch.int32, device=device) for _ in range(2)]
+        self.val = [torch.empty((n_q, k), dtype=torch.float32, device=device) for _ in range(2)]
+        self.O = [torch.empty((n_q, T, h_q, d), dtype=td, device=device) for _ in range(2)]
+        self.route_stream = torch.cuda.Stream(device=device)
+        self.attend_stream = torch.cuda.Stream(device=device)
+        self.selected = [torch.cuda.Event() for _ in range(2)]
+        self.done = [torch.cuda.Event() for _ in range(2)]
+        self.issued = 0
+
+    def step(self, QR, Q, K_loc, V_loc) -> int:
+        """Issue one decode step; returns its output slot.  The inputs must stay
+        alive (and unchanged) until the step has run."""
+        s = self.issued % 2
+        c = self.bank.c
+        rs, at = self.route_stream, self.attend_stream
+        rs.wait_stream(torch.cuda.current_stream())  # the caller's inputs are ready
+        if self.issued >= 2:
+            rs.wait_event(self.done[s])  # attend(step - 2) has read idx[s]
+        _lib.msa_route_score(c, QR, self.n_q, self.t_r, self.s_doc[s], None, self.ws_route, self.ws_route_n, rs)
+        _lib.msa_topk(self.s_doc[s], self.n_q, c.n_docs, self.k, self.idx[s], self.val[s], self.ws_topk,
+                      self.ws_topk_n, rs)
+        self.selected[s].record(rs)
+        at.wait_event(self.selected[s])
+        _lib.msa_sparse_attend(c, Q, K_loc, V_loc, self.n_q, self.T, self.L_loc, self.h_q, self.idx[s], self.k,
+                               self.pos0, self.scale, self.rope.c, self.O[s], self.ws_attend, self.ws_attend_n, at)
+        self.done[s].record(at)
+        self.issued += 1
+        return s
+
+    def synchronize(self) -> None:
+        self.route_stream.synchronize()
+        self.attend_stream.synchronize()

@@ -63,7 +63,7 @@ MIS = _Fake(0x10004)    # misaligned
 
 def _bank(**over):
     lay = msa.msa_bank_layout([512] * 4, 128)
-    b = L.MsaBank(L.MSA_BF16, 4, 128, 8, 128, 8, 128, 512, 4, 0, lay["n_chunks"], A.addr, A.addr, None, None,
+    b = L.MsaBank(L.MSA_BF16, 4, 128, 8, 128, 8, 128, 512, 4, 0, 0, 0, lay["n_chunks"], A.addr, A.addr, None, None,
                   A.addr, A.addr, A.addr, A.addr, A.addr)
     for k, v in over.items():
         setattr(b, k, v)
