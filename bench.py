@@ -209,6 +209,81 @@ def bench_interleave(args) -> int:
     return 0
 
 
+def bench_append(args) -> int:
+    """Incremental update of the 100M-token bank: encode the first 90% of the
+    documents into a bank with room for all, append the rest, pool only the
+    appended range; report the pooling rate of the appended range and the
+    decode layer time before and after (the scan grows with the bank)."""
+    import numpy as np
+    import torch
+
+    from synth import device as sdev, workloads as W
+    from long_context_memory_msa_amd import _lib as L, memory as M, offline
+
+    dev = torch.device("cuda:0")
+    w = W.make_workload(3, bank_tokens=args.bank_tokens)
+    qi = W.query_inputs(w)
+    uhat = torch.from_numpy(W.gold_uhat(w, qi["QR"])).to(dev)
+    td = M.TORCH_DTYPE[w.dtype]
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(td).contiguous()
+
+    QR = up(qi["QR"][:, w.L_loc - w.T_route:w.L_loc])
+    Q = up(qi["Q"][:, w.L_loc - w.T:w.L_loc])
+    Kl = up(qi["K_loc"][:, :w.L_loc])
+    Vl = up(qi["V_loc"][:, :w.L_loc])
+    n0 = int(w.n_docs * 0.9)
+    bank = M.Bank(w.doc_lens[:n0], w.chunk, w.h_kv, w.d, w.h_r, w.d_r, w.dtype, dev, cap_docs=w.n_docs,
+                  cap_chunks=w.n_chunks)
+    rope = M.Rope(w.max_pos, w.d, w.rope_base, dev)
+    fill = lambda a, b, K, V, KR: sdev.fill_raw_slab(w, 0, a, b, K, V, KR, uhat)
+    offline.encode_bank(bank, rope, fill, args.slab_tokens, w.h_kv, w.d, w.h_r, w.d_r)
+    scale = L.default_scale(w.d)
+
+    def layer_ms():
+        O_ = torch.empty((w.n_q, w.T, w.h_q, w.d), dtype=td, device=dev)
+        idx = torch.empty((w.n_q, w.k), dtype=torch.int32, device=dev)
+        val = torch.empty((w.n_q, w.k), dtype=torch.float32, device=dev)
+        nb = L.msa_layer_workspace_bytes(bank.c, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k)
+        ws = M.workspace(nb, dev)
+        run = lambda ev=None: L.msa_layer_forward(bank.c, Q, Kl, Vl, QR, w.n_q, w.T, w.T_route, w.L_loc, w.h_q,
+                                                  w.k, w.pos0, scale, rope.c, O_, idx, val, None, ws, nb, ev)
+        for _ in range(3):
+            run()
+        ev = Events(4 * 10)
+        for i in range(10):
+            run(ev.h[4 * i:4 * i + 4])
+        torch.cuda.synchronize()
+        t = statistics.median(ev.ms(ev.h[4 * i], ev.h[4 * i + 3]) for i in range(10))
+        ev.close()
+        return t, idx.cpu().numpy()
+
+    before, _ = layer_ms()
+    a, b = bank.append(w.doc_lens[n0:])
+    enc = offline.encode_bank(bank, rope, fill, args.slab_tokens, w.h_kv, w.d, w.h_r, w.d_r, time_slabs=True,
+                              docs=(a, b))
+    after, idx = layer_ms()
+    n_new = int(w.doc_tok_off[b] - w.doc_tok_off[a])
+    ch_new = int(w.doc_chunk_off[b] - w.doc_chunk_off[a])
+    pooled = ch_new * ((2 * w.h_kv * w.d + w.h_r * w.d_r) * 2 + 4 * w.h_r + 4)
+    secs = sum(enc["seconds"])
+    gold_ok = float(np.mean([set(w.gold[q].tolist()) <= set(idx[q].tolist()) for q in range(w.n_q)]))
+    rec = {
+        "metric": "incremental bank append: pooling rate of the appended documents",
+        "value": (sum(enc["raw_bytes"]) + pooled) / secs / 1e9,
+        "unit": "GB/s",
+        "appended": {"docs": b - a, "tokens": n_new, "chunks": ch_new, "pool_ms": secs * 1e3,
+                     "tokens_per_s": n_new / secs},
+        "layer_ms_before": before, "layer_ms_after": after,
+        "bank_tokens_before": int(w.doc_tok_off[a]), "bank_tokens_after": int(w.doc_tok_off[b]),
+        "gold_recovered_after": gold_ok,
+        "data": "synthetic",
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def bench_tiered(args) -> int:
     """The 100M-token decode layer with a tiered bank: pooled keys/values in
     pinned host memory (read by the attention over the host link), router keys
@@ -310,10 +385,11 @@ def main() -> int:
                     help="oracle baseline sample: first N documents (-1 = the whole bank, 0 = skip)")
     ap.add_argument("--bank-tokens", type=int, default=None, help="smaller bank for a quick look (not the metric)")
     ap.add_argument("--slab-tokens", type=int, default=8_000_000)
-    ap.add_argument("--workload", choices=["decode100m", "interleave", "tiered"], default="decode100m",
+    ap.add_argument("--workload", choices=["decode100m", "interleave", "tiered", "append"], default="decode100m",
                     help="decode100m: the headline layer (default); interleave: 18 routed layers x 10M tokens, "
                          "3 Memory Interleave rounds (MFMA-bound prefill report); tiered: the decode layer with "
-                         "Kbar/Vbar in host memory, two-stream pipeline")
+                         "Kbar/Vbar in host memory, two-stream pipeline; append: the last 10%% of the documents "
+                         "appended to an encoded bank")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -345,6 +421,8 @@ def main() -> int:
         return bench_interleave(args)
     if args.workload == "tiered":
         return bench_tiered(args)
+    if args.workload == "append":
+        return bench_append(args)
     w = W.make_workload(3, bank_tokens=args.bank_tokens)
     print(f"[bench] {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr, flush=True)
 
