@@ -209,6 +209,51 @@ def bench_interleave(args) -> int:
     return 0
 
 
+def bench_project(args) -> int:
+    """Router projection GEMM (Y = X W^T, bf16, fp32 accumulation): the
+    encoding-time projection of a 256K-token slab of memory hidden states
+    (hidden 2560 -> router 4 x 256) and the decode-time projection of 16 query
+    tokens; MFMA roofline of the slab GEMM."""
+    import torch
+
+    from synth import rng, workloads as W
+    from long_context_memory_msa_amd import _lib as L
+
+    dev = torch.device("cuda:0")
+    hidden, out = 2560, 1024
+    res = {}
+    for name, rows in (("encode_slab", 262144), ("decode_query", 16)):
+        X = torch.from_numpy(W.hidden_states(9, rng.ROLE_HID_MEM, rows, hidden)).to(dev).to(torch.bfloat16)
+        Wt = torch.from_numpy(W.projector_weights(9, rng.ROLE_W_KR, hidden, out)).to(dev).to(torch.bfloat16)
+        Y = torch.empty((rows, out), dtype=torch.bfloat16, device=dev)
+        for _ in range(max(1, args.warmup)):
+            L.msa_router_project(X, Wt, rows, hidden, out, Y)
+        torch.cuda.synchronize()
+        n = max(5, args.steps)
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for i in range(n):
+            e0[i].record()
+            L.msa_router_project(X, Wt, rows, hidden, out, Y)
+            e1[i].record()
+        torch.cuda.synchronize()
+        ms = statistics.median(e0[i].elapsed_time(e1[i]) for i in range(n))
+        flop = 2.0 * rows * hidden * out
+        res[name] = {"rows": rows, "ms": ms, "tflops": flop / (ms * 1e-3) / 1e12,
+                     "mfma_frac": flop / (ms * 1e-3) / 2.5e15}
+    rec = {
+        "metric": "router projection GEMM (hidden 2560 -> 4 x 256), bf16 MFMA",
+        "value": res["encode_slab"]["tflops"],
+        "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": res["encode_slab"]["tflops"], "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": res["encode_slab"]["mfma_frac"]},
+        "cases": res,
+        "data": "synthetic",
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def bench_append(args) -> int:
     """Incremental update of the 100M-token bank: encode the first 90% of the
     documents into a bank with room for all, append the rest, pool only the
@@ -385,11 +430,12 @@ def main() -> int:
                     help="oracle baseline sample: first N documents (-1 = the whole bank, 0 = skip)")
     ap.add_argument("--bank-tokens", type=int, default=None, help="smaller bank for a quick look (not the metric)")
     ap.add_argument("--slab-tokens", type=int, default=8_000_000)
-    ap.add_argument("--workload", choices=["decode100m", "interleave", "tiered", "append"], default="decode100m",
+    ap.add_argument("--workload", choices=["decode100m", "interleave", "tiered", "append", "project"],
+                    default="decode100m",
                     help="decode100m: the headline layer (default); interleave: 18 routed layers x 10M tokens, "
                          "3 Memory Interleave rounds (MFMA-bound prefill report); tiered: the decode layer with "
                          "Kbar/Vbar in host memory, two-stream pipeline; append: the last 10%% of the documents "
-                         "appended to an encoded bank")
+                         "appended to an encoded bank; project: the router projection GEMM")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -423,6 +469,8 @@ def main() -> int:
         return bench_tiered(args)
     if args.workload == "append":
         return bench_append(args)
+    if args.workload == "project":
+        return bench_project(args)
     w = W.make_workload(3, bank_tokens=args.bank_tokens)
     print(f"[bench] {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr, flush=True)
 

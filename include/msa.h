@@ -104,7 +104,7 @@ typedef struct msa_bank {
   int32_t h_kv;
   int32_t d;
   int32_t h_r;
-  int32_t d_r;
+  int32_t d_r;         /* 64, 128, or 256 (bf16); h_r * d_r <= 1024 */
   int32_t max_doc_len;
   int32_t max_doc_chunks;
   int32_t chunk_cap;   /* row capacity of kbar/vbar, >= n_chunks; 0 = n_chunks */
@@ -171,10 +171,27 @@ int msa_rope_table(float *cos, float *sin, int32_t max_pos, int32_t d, double ba
  * first token of doc_begin.  Needs the host offset arrays in *b.
  * Errors: MSA_ERR_ARG (null/misaligned, bad range, inconsistent layout,
  * rope too short for max_doc_len or wrong d), MSA_ERR_UNSUPPORTED (dtype,
- * d or d_r not 64/128).
+ * d not 64/128, d_r not 64/128/256 -- 256, a router twice the head width, for
+ * bf16 banks -- or h_r * d_r > 1024).
  */
 int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void *KR, int32_t doc_begin,
                     int32_t doc_end, const msa_rope *rope, void *stream);
+
+/*
+ * Router projection ([HD] core architecture of the learnable memory routing
+ * layer: projectors map hidden states to the router query Q^R and, at
+ * encoding time, to the router key K^R of every memory token; [HD] parameter
+ * advice: router width 2-4x the head dimension):
+ *   Y[r][o] = sum_i X[r][i] * W[o][i]
+ * X [rows][hidden], W [out][hidden] (one row per output feature, i.e.
+ * h_r * d_r rows), Y [rows][out]; all bf16, accumulated in fp32 and rounded
+ * once (nearest even).  rows >= 0 (0 enqueues nothing), hidden a positive
+ * multiple of 64, out a positive multiple of 128.  Y reshaped as
+ * [rows][h_r][d_r] is the QR argument of msa_route_score, or the KR slab of
+ * msa_pool_memory.  Errors: MSA_ERR_ARG (null/misaligned pointers, sizes).
+ */
+int msa_router_project(const void *X, const void *W, int64_t rows, int32_t hidden, int32_t out, void *Y,
+                       void *stream);
 
 /* Workspace bytes msa_route_score needs for these sizes (0 = none; 0 on invalid sizes). */
 size_t msa_route_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t t_r);

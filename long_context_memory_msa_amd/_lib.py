@@ -63,6 +63,7 @@ def _load():
         "msa_abi_version": ([], ctypes.c_int),
         "msa_last_error": ([], ctypes.c_char_p),
         "msa_device_pointer": ([P, P], ctypes.c_int),
+        "msa_router_project": ([P, P, I64, I32, I32, P, P], ctypes.c_int),
         "msa_bank_layout": ([P, I32, I32, P, P, P, P, P], ctypes.c_int),
         "msa_rope_table": ([P, P, I32, I32, D, P], ctypes.c_int),
         "msa_pool_memory": ([bank_p, P, P, P, I32, I32, rope_p, P], ctypes.c_int),
@@ -148,6 +149,10 @@ def msa_rope_table(cos, sin, max_pos: int, d: int, base: float = 10000.0, stream
 def msa_pool_memory(bank: MsaBank, K, V, KR, doc_begin: int, doc_end: int, rope: MsaRope, stream=None) -> None:
     _check(_lib.msa_pool_memory(ctypes.byref(bank), _ptr(K), _ptr(V), _ptr(KR), doc_begin, doc_end,
                                 ctypes.byref(rope), _stream(stream)))
+
+
+def msa_router_project(X, W, rows: int, hidden: int, out: int, Y, stream=None) -> None:
+    _check(_lib.msa_router_project(_ptr(X), _ptr(W), rows, hidden, out, _ptr(Y), _stream(stream)))
 
 
 def msa_route_workspace_bytes(bank: MsaBank, n_q: int, t_r: int) -> int:

@@ -19,7 +19,7 @@ OBJ_DIR = ROOT / "_build" / "msa"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "pool.hip", "route.hip", "route_wide.hip", "topk.hip", "attend.hip"]
+SOURCES = ["api.cpp", "pool.hip", "route.hip", "route_wide.hip", "topk.hip", "attend.hip", "project.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # never emit packed fp32 arithmetic (v_pk_*_f32)

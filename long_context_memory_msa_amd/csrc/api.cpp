@@ -54,7 +54,9 @@ int check_bank(const msa_bank *b) {
   if (b->chunk < 1) return fail(MSA_ERR_ARG, "chunk = %d", b->chunk);
   if (b->h_kv < 1) return fail(MSA_ERR_ARG, "h_kv = %d", b->h_kv);
   if (b->d != 64 && b->d != 128) return fail(MSA_ERR_UNSUPPORTED, "head dim d = %d (64 or 128)", b->d);
-  if (b->d_r != 64 && b->d_r != 128) return fail(MSA_ERR_UNSUPPORTED, "router dim d_r = %d (64 or 128)", b->d_r);
+  if (b->d_r != 64 && b->d_r != 128 && b->d_r != 256)
+    return fail(MSA_ERR_UNSUPPORTED, "router dim d_r = %d (64, 128, or 256 for bf16)", b->d_r);
+  if (b->d_r == 256 && b->dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "router dim 256 needs a bf16 bank");
   if (b->h_r != 1 && b->h_r != 2 && b->h_r != 4 && b->h_r != 8 && b->h_r != 16)
     return fail(MSA_ERR_UNSUPPORTED, "router heads h_r = %d (1, 2, 4, 8 or 16)", b->h_r);
   if (b->h_r * b->d_r > 1024) return fail(MSA_ERR_UNSUPPORTED, "h_r * d_r = %d > 1024", b->h_r * b->d_r);
@@ -204,6 +206,24 @@ extern "C" {
 int msa_abi_version(void) { return MSA_ABI_VERSION; }
 
 const char *msa_last_error(void) { return g_err.c_str(); }
+
+int msa_router_project(const void *X, const void *W, int64_t rows, int32_t hidden, int32_t out, void *Y,
+                       void *stream) {
+  try {
+    CHECK_PTR(X, 16, "X");
+    CHECK_PTR(W, 16, "W");
+    CHECK_PTR(Y, 16, "Y");
+    if (rows < 0) return fail(MSA_ERR_ARG, "rows = %lld", (long long)rows);
+    if (hidden < 64 || hidden % 64) return fail(MSA_ERR_ARG, "hidden = %d (a positive multiple of 64)", hidden);
+    if (out < 128 || out % 128) return fail(MSA_ERR_ARG, "out = %d (a positive multiple of 128)", out);
+    if ((rows + 127) / 128 * (int64_t)(out / 128) > ((int64_t)1 << 31) - 1024)
+      return fail(MSA_ERR_ARG, "rows * out too large");
+    hipError_t e = msa::launch_project(X, W, rows, hidden, out, Y, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : dev_fail(e, "router_project");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
 
 int msa_device_pointer(const void *host, void **dev) {
   if (!host || !dev) return fail(MSA_ERR_ARG, "null pointer");

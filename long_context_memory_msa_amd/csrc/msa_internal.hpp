@@ -104,6 +104,11 @@ struct TopkSrc {
 hipError_t launch_topk(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,
                        hipStream_t s);
 
+// ---- router projection -------------------------------------------------------
+// Y[rows][out] = X[rows][hidden] W[out][hidden]^T, bf16 in and out, fp32 accumulation;
+// hidden % 64 == 0, out % 128 == 0
+hipError_t launch_project(const void *X, const void *W, int64_t rows, int hidden, int out, void *Y, hipStream_t s);
+
 // ---- sparse attention ------------------------------------------------------
 struct AttendArgs {
   int dtype;

@@ -155,7 +155,13 @@ hipError_t pool_dispatch(const PoolArgs &a, hipStream_t s) {
   if (a.d == 64 && a.d_r == 64) hipLaunchKernelGGL((pool_kernel<T, 64, 64>), grid, block, 0, s, a);
   else if (a.d == 64 && a.d_r == 128) hipLaunchKernelGGL((pool_kernel<T, 64, 128>), grid, block, 0, s, a);
   else if (a.d == 128 && a.d_r == 64) hipLaunchKernelGGL((pool_kernel<T, 128, 64>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((pool_kernel<T, 128, 128>), grid, block, 0, s, a);
+  else if (a.d == 128 && a.d_r == 128) hipLaunchKernelGGL((pool_kernel<T, 128, 128>), grid, block, 0, s, a);
+  else if constexpr (sizeof(T) == 2) {  // router width 256: bf16 banks
+    if (a.d == 64) hipLaunchKernelGGL((pool_kernel<T, 64, 256>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((pool_kernel<T, 128, 256>), grid, block, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,151 @@
+// Router projection Y = X W^T: hidden states to router queries or keys.
+//
+// The router's projectors map the backbone's hidden states to the router
+// query Q^R (for the current tokens) and the router key K^R (for every memory
+// token, at encoding time) -- hotdry blog, core architecture of the learnable
+// memory routing layer; its parameter advice puts the router width at 2-4x
+// the head dimension.  X [rows][hidden] bf16, W [out][hidden] bf16 (one row
+// per output feature), Y [rows][out] bf16 rounded once from an fp32
+// accumulation.
+//
+// A bf16 GEMM with both operands contiguous along K:
+//  * a workgroup owns 128 rows x 128 outputs; four waves of 64 x 64 on
+//    v_mfma_f32_16x16x32_bf16;
+//  * the K loop runs in stages of 64 elements (128 bytes per row) filled by
+//    direct-to-LDS loads into swizzled rows, double-buffered (separate LDS
+//    variables per buffer, so the compiler does not wait for the fill in
+//    flight), one barrier per stage;
+//  * output tiles of one row tile share an XCD (blockIdx % 8), so the row
+//    tile is re-read from that XCD's L2.
+#include <algorithm>
+
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int PT = 128;  // rows (and outputs) per workgroup
+constexpr int SK = 64;   // K elements per stage
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ void fill16(const bf16_t *g, bf16_t *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
+}
+
+constexpr int VM0 = 0 | (7 << 4) | (15 << 8);            // vmcnt(0)
+constexpr int LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0)
+
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(VM0);
+  __builtin_amdgcn_s_waitcnt(LGKM0);
+  __builtin_amdgcn_s_barrier();
+}
+
+__global__ __launch_bounds__(256, 2) void project_kernel(const bf16_t *X, const bf16_t *W, int64_t rows, int hidden,
+                                                         int out, bf16_t *Y, int n_rtiles, int n_otiles) {
+  __shared__ __align__(16) bf16_t sA0[PT * SK], sA1[PT * SK];
+  __shared__ __align__(16) bf16_t sB0[PT * SK], sB1[PT * SK];
+
+  // tile order: output tiles of one row tile share blockIdx % 8 (one XCD)
+  const int b = blockIdx.x;
+  const int r8 = b / 8;
+  const int o_tile = r8 % n_otiles;
+  const int r_tile = (r8 / n_otiles) * 8 + (b % 8);
+  if (r_tile >= n_rtiles) return;  // padding workgroup: exits as a whole before any barrier
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, G = lane >> 4;
+  const int wr = wave & 1, wc = wave >> 1;
+  const int64_t row0 = (int64_t)r_tile * PT;
+  const int o0 = o_tile * PT;
+  const int rows_here = (int)std::min<int64_t>(PT, rows - row0);
+  const bf16_t *xt = X + row0 * hidden;
+  const bf16_t *wt = W + (int64_t)o0 * hidden;
+
+  // fill of a stage: wave w writes rows 32w .. 32w+31 of each operand; in load
+  // p, lane L writes row 32w + 8p + L/8 at physical slot L%8 = logical slot
+  // (L%8) ^ swz(row); rows past the end read the last valid row (discarded)
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = 32 * wave + 8 * p + lane / 8;
+    const int slot = (lane % 8) ^ swz(row);
+    aoff[p] = (uint32_t)(std::min(row, rows_here - 1) * hidden + slot * 8);
+    boff[p] = (uint32_t)(row * hidden + slot * 8);
+  }
+  auto fill = [&](bf16_t *dA, bf16_t *dB, int k0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      fill16(xt + aoff[p] + k0, dA + (32 * wave + 8 * p) * SK);
+      fill16(wt + boff[p] + k0, dB + (32 * wave + 8 * p) * SK);
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+  // k-step ks pairs logical slot 2G + ks of a row of X and of W
+  auto multiply = [&](const bf16_t *sA, const bf16_t *sB) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = 64 * wr + 16 * i + col, rb = 64 * wc + 16 * i + col;
+        fa[i] = *reinterpret_cast<const bf16x8 *>(sA + ra * SK + ((2 * G + ks) ^ swz(ra)) * 8);
+        fb[i] = *reinterpret_cast<const bf16x8 *>(sB + rb * SK + ((2 * G + ks) ^ swz(rb)) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
+    }
+  };
+
+  const int n_stages = hidden / SK;
+  fill(sA0, sB0, 0);
+  stage_barrier();
+#pragma unroll 1
+  for (int st = 0; st < n_stages; st += 2) {
+    if (st + 1 < n_stages) fill(sA1, sB1, (st + 1) * SK);
+    multiply(sA0, sB0);
+    stage_barrier();
+    if (st + 1 < n_stages) {
+      if (st + 2 < n_stages) fill(sA0, sB0, (st + 2) * SK);
+      multiply(sA1, sB1);
+      stage_barrier();
+    }
+  }
+
+  // acc[i][j]: rows 64 wr + 16 i + 4 G + e, outputs 64 wc + 16 j + col
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 64 * wr + 16 * i + 4 * G + e;
+      if (r < rows_here) {
+        bf16_t *yrow = Y + (row0 + r) * out + o0 + 64 * wc + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yrow[16 * j] = bf16_t{f32_to_bf16(acc[i][j][e])};
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_project(const void *X, const void *W, int64_t rows, int hidden, int out, void *Y, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int n_rtiles = (int)((rows + PT - 1) / PT), n_otiles = out / PT;
+  const int64_t grid = 8 * (int64_t)n_otiles * ((n_rtiles + 7) / 8);
+  hipLaunchKernelGGL(project_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(X),
+                     static_cast<const bf16_t *>(W), rows, hidden, out, static_cast<bf16_t *>(Y), n_rtiles, n_otiles);
+  return hipGetLastError();
+}
+
+}  // namespace msa

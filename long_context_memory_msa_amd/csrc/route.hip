@@ -350,7 +350,9 @@ hipError_t route_by_hr(const RouteArgs &a, hipStream_t s) {
     case 1: return route_mode<T, 1, DR>(a, s);
     case 2: return route_mode<T, 2, DR>(a, s);
     case 4: return route_mode<T, 4, DR>(a, s);
-    case 8: return route_mode<T, 8, DR>(a, s);
+    case 8:
+      if constexpr (DR <= 128) return route_mode<T, 8, DR>(a, s);
+      return hipErrorInvalidValue;
     default:
       if constexpr (DR == 64) return route_mode<T, 16, DR>(a, s);
       return hipErrorInvalidValue;
@@ -395,6 +397,7 @@ hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s) {
   if (a.n_chunks == 0) return hipSuccess;
   if (!a.edges && a.qinv && route_use_wide(a.dtype, a.h_r, a.d_r, a.t_r)) return launch_route_wide(a, s);
   if (a.dtype == 0) return a.d_r == 64 ? route_by_hr<float, 64>(a, s) : route_by_hr<float, 128>(a, s);
+  if (a.d_r == 256) return route_by_hr<bf16_t, 256>(a, s);  // a router twice the head width
   return a.d_r == 64 ? route_by_hr<bf16_t, 64>(a, s) : route_by_hr<bf16_t, 128>(a, s);
 }
 

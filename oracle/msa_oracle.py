@@ -28,6 +28,9 @@ Readings taken where the pages are silent (each is also listed in the design doc):
   R9 attention scale 1/sqrt(d), no bias on pooled keys; memory keys are visible
      to every query token, local keys causally; q-head h reads KV head
      h // (H_q / H_kv).
+  R10 the router projectors are plain linear maps without bias (Q^R = x W_QR^T,
+     K^R = h W_KR^T per token, before pooling); their outputs are stored in
+     the bank dtype (rounded once) like every other stored tensor.
 
 Parity is pinned for every function by tests/test_oracle_pins.py; none is
 "parity unpinned".
@@ -66,6 +69,17 @@ def round_store(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Router projection ([HD] core architecture of the learnable memory routing
+# layer: the router projectors map hidden states to Q^R and, per memory token,
+# to K^R; [HD] parameter advice: router width 2-4x the head dimension).
+def project(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Y[..., o] = sum_i X[..., i] * W[o, i] in fp64 (W: one row per output
+    feature), unrounded; R10."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    return X @ W.T
+
+
 # RoPE ([LH] Component 2, document-wise and global RoPE; [HD] key engineering
 # details, position encoding).  Formula not printed on the pages: reading R4.
 def rope_theta(d: int, base: float = 10000.0) -> np.ndarray:

@@ -40,6 +40,7 @@ _CENTRE = 262140  # 2 * (4 * 65535) / 2
 ROLE_KR, ROLE_K, ROLE_V, ROLE_QR, ROLE_Q, ROLE_KLOC, ROLE_VLOC = range(7)
 ROLE_SCORES = 7  # synthetic document scores for isolated top-k tests
 ROLE_POOLED_KR, ROLE_POOLED_K, ROLE_POOLED_V = 8, 9, 10  # pooled-shape timing inputs
+ROLE_HID_MEM, ROLE_HID_Q, ROLE_W_KR, ROLE_W_QR = 11, 12, 13, 14  # router-projector inputs
 
 
 def _u64(x) -> np.ndarray:

@@ -242,3 +242,18 @@ def scores_for_topk(seed: int, n_q: int, n_docs: int, tie_frac: float = 0.25) ->
     m = g.random((n_q, n_docs)) < tie_frac
     s = np.where(m, np.round(s * 8.0) / 8.0, s).astype(np.float32)
     return s
+
+
+# ---- router-projector inputs (hidden states and seeded projector weights) ----
+def hidden_states(seed: int, role: int, n: int, hidden: int, layer: int = 0) -> np.ndarray:
+    """bf16-stored N(0,1) hidden states [n][hidden] (memory tokens or queries)."""
+    key = rng.stream_key(seed, role, layer)
+    return rng.normal_stored(key, 0, n * hidden, "bf16").reshape(n, hidden)
+
+
+def projector_weights(seed: int, role: int, hidden: int, out: int, layer: int = 0) -> np.ndarray:
+    """bf16-stored projector W [out][hidden] with entries N(0, 1/hidden): the
+    projected features of N(0,1) hidden states are about N(0,1)."""
+    key = rng.stream_key(seed, role, layer)
+    w = rng.normal_stored(key, 0, out * hidden, "f32").reshape(out, hidden) * np.float32(1.0 / np.sqrt(hidden))
+    return rng.store_round(w.astype(np.float32), "bf16")

@@ -96,7 +96,9 @@ def test_bank_validation():
                        ({"h_r": 3}, L.MSA_ERR_UNSUPPORTED), ({"n_docs": 0}, L.MSA_ERR_ARG),
                        ({"max_doc_chunks": 9}, L.MSA_ERR_ARG), ({"kbar": None}, L.MSA_ERR_ARG),
                        ({"krbar": MIS.addr}, L.MSA_ERR_ARG), ({"n_chunks": 1}, L.MSA_ERR_ARG),
-                       ({"chunk_cap": 15}, L.MSA_ERR_ARG), ({"chunk_cap": -1}, L.MSA_ERR_ARG)):
+                       ({"chunk_cap": 15}, L.MSA_ERR_ARG), ({"chunk_cap": -1}, L.MSA_ERR_ARG),
+                       ({"d_r": 256, "h_r": 4, "dtype": L.MSA_F32}, L.MSA_ERR_UNSUPPORTED),
+                       ({"d_r": 256}, L.MSA_ERR_UNSUPPORTED), ({"d_r": 512, "h_r": 2}, L.MSA_ERR_UNSUPPORTED)):
         assert _code(msa.msa_route_score, _bank(**over), A, 1, 1, A, None, A, 1 << 30, stream=0) == code, over
 
 
@@ -120,6 +122,21 @@ def test_bank_capacity_host_side():
     with pytest.raises(ValueError):
         b.append([0])
     assert isinstance(b.kbar, torch.Tensor)
+
+
+def test_router_project_validation():
+    ok = dict(X=A, W=A, rows=16, hidden=640, out=1024, Y=A)
+
+    def call(**over):
+        a = {**ok, **over}
+        return _code(msa.msa_router_project, a["X"], a["W"], a["rows"], a["hidden"], a["out"], a["Y"], 0)
+
+    assert call(X=None) == L.MSA_ERR_ARG
+    assert call(Y=MIS) == L.MSA_ERR_ARG
+    assert call(rows=-1) == L.MSA_ERR_ARG
+    assert call(hidden=100) == L.MSA_ERR_ARG      # not a multiple of 64
+    assert call(out=200) == L.MSA_ERR_ARG         # not a multiple of 128
+    assert call(hidden=0) == L.MSA_ERR_ARG
 
 
 def test_route_validation():

@@ -141,13 +141,15 @@ def test_route_isolated(device, name, t_r, n_q):
     assert torch.equal(s_doc, s_doc2)
 
 
-# every router head shape the ABI admits (h_r in 1..16, d_r 64 / 128, fp32 and
-# bf16), few rows (decode scan) and many rows per query (tiled scan), on a small
+# every router head shape the ABI admits (h_r in 1..16, d_r 64 / 128 / 256 --
+# 256 for bf16 --, fp32 and bf16), few rows (decode scan) and many rows per
+# query (tiled scan), on a small
 # ragged bank of the prefill workload's document law (several 128-chunk tiles)
 @pytest.mark.parametrize("dtype,h_r,d_r,t_r,n_q", [
     ("bf16", 1, 128, 48, 2), ("bf16", 2, 128, 32, 3), ("bf16", 4, 128, 64, 1), ("bf16", 2, 128, 1, 16),
     ("bf16", 4, 64, 1, 5), ("bf16", 16, 64, 32, 2), ("bf16", 16, 64, 1, 16), ("f32", 16, 64, 16, 1),
-    ("f32", 4, 128, 5, 2), ("f32", 8, 128, 48, 1)])
+    ("f32", 4, 128, 5, 2), ("f32", 8, 128, 48, 1),
+    ("bf16", 4, 256, 1, 16), ("bf16", 2, 256, 48, 2), ("bf16", 1, 256, 16, 3)])
 def test_route_head_shapes(device, dtype, h_r, d_r, t_r, n_q):
     w = _wl(2, 60_000)
     # one small attention head: K/V do not enter the routing

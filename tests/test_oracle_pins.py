@@ -345,3 +345,34 @@ def test_planted_gold_recovered_decode_shape():
     res = _oracle_layer(w)
     for q in range(w.n_q):
         assert set(w.gold[q].tolist()) <= set(res["idx"][q].tolist())
+
+
+# ---- router projection (R10) -------------------------------------------------
+def test_project_brute_force_tiny():
+    rng_ = np.random.default_rng(11)
+    X = rng_.standard_normal((3, 5))
+    Wt = rng_.standard_normal((4, 5))
+    want = np.array([[sum(X[r, i] * Wt[o, i] for i in range(5)) for o in range(4)] for r in range(3)])
+    assert np.allclose(O.project(X, Wt), want, rtol=1e-14, atol=1e-14)
+
+
+def test_project_identity_permutation_and_scaling_are_exact():
+    rng_ = np.random.default_rng(12)
+    X = O.round_bf16(rng_.standard_normal((7, 128)))
+    assert np.array_equal(O.project(X, np.eye(128)), X)
+    perm = rng_.permutation(128)
+    P = np.eye(128)[perm] * 0.25                     # output o reads input perm[o], scaled by 2^-2
+    assert np.array_equal(O.project(X, P), X[:, perm] * 0.25)
+
+
+def test_project_is_linear_and_batches_leading_axes():
+    rng_ = np.random.default_rng(13)
+    X1, X2 = rng_.standard_normal((2, 3, 64)), rng_.standard_normal((2, 3, 64))
+    Wt = rng_.standard_normal((128, 64))
+    Y = O.project(2.0 * X1 - 3.0 * X2, Wt)
+    assert np.allclose(Y, 2.0 * O.project(X1, Wt) - 3.0 * O.project(X2, Wt), atol=1e-11)
+    assert O.project(X1, Wt).shape == (2, 3, 128)
+    # a zero row of W gives a zero output feature
+    Wz = Wt.copy()
+    Wz[5] = 0.0
+    assert np.all(O.project(X1, Wz)[..., 5] == 0.0)
