@@ -17,6 +17,13 @@
 //    flight), one barrier per stage;
 //  * output tiles of one row tile share an XCD (blockIdx % 8), so the row
 //    tile is re-read from that XCD's L2.
+//
+// A few rows (a decode step's queries) leave that tiling with out/128
+// workgroups walking the whole K loop one after another; there the product is
+// a stream of W (out x hidden) with X held in L2, and it runs skinny instead:
+// one workgroup per 16 outputs, its eight waves splitting K into contiguous
+// ranges (16-byte loads straight into MFMA operands, no LDS staging), the
+// eight partial 16 x 16 tiles summed through LDS.
 #include <algorithm>
 
 #include "msa_device.hpp"
@@ -30,6 +37,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int PT = 128;  // rows (and outputs) per workgroup
 constexpr int SK = 64;   // K elements per stage
+// row counts up to this take the skinny kernel (at most 4 row tiles of 16)
+#ifndef MSA_PROJ_SKINNY_ROWS
+#define MSA_PROJ_SKINNY_ROWS 64
+#endif
+constexpr int SKINNY_ROWS = MSA_PROJ_SKINNY_ROWS;
+static_assert(SKINNY_ROWS <= 64, "skinny projection holds at most 4 row tiles");
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -137,10 +150,82 @@ __global__ __launch_bounds__(256, 2) void project_kernel(const bf16_t *X, const 
     }
 }
 
+// rows <= 16 * MT; grid = out / 16 workgroups of 8 waves
+template <int MT>
+__global__ __launch_bounds__(512) void project_skinny_kernel(const bf16_t *X, const bf16_t *W, int rows, int hidden,
+                                                             int out, bf16_t *Y) {
+  __shared__ f32x4 red[8][MT][64];
+  // The wave index goes through a scalar register so the k-range and batch
+  // bounds below are scalar and every branch around an MFMA is a scalar
+  // branch: MFMA ignores EXEC, so an MFMA left under an all-false lane mask
+  // would still accumulate stale operands.
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, G = lane >> 4;
+  const int o0 = blockIdx.x * 16;
+  // k-step s covers elements 32 s .. 32 s + 31; lane group G takes 8 of them
+  const int n_steps = hidden / 32;
+  const int s0 = n_steps * wave / 8, s1 = n_steps * (wave + 1) / 8;
+  const bf16_t *wrow = W + (int64_t)(o0 + col) * hidden + 8 * G;
+  const bf16_t *xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xrow[m] = X + (int64_t)std::min(16 * m + col, rows - 1) * hidden + 8 * G;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = zero4();
+  // batches of U k-steps: every load of a batch is issued before its first MFMA
+  constexpr int U = MT <= 2 ? 8 : 4;
+  auto batch = [&](int st, int n) {
+    bf16x8 b[U], a[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < n) {
+        b[u] = *reinterpret_cast<const bf16x8 *>(wrow + 32 * (st + u));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a[u][m] = *reinterpret_cast<const bf16x8 *>(xrow[m] + 32 * (st + u));
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < n)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = mfma16(a[u][m], b[u], acc[m]);
+  };
+  int st = s0;
+#pragma unroll 1
+  for (; st + U <= s1; st += U) batch(st, U);
+  if (st < s1) batch(st, s1 - st);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+  __syncthreads();
+  // acc[m] of lane l, element e: row 16 m + 4 (l / 16) + e, output o0 + l % 16;
+  // thread t takes (m, l / 16, e) = t / 16 and output t % 16
+  for (int t = threadIdx.x; t < MT * 256; t += 512) {
+    const int c = t & 15, e = (t >> 4) & 3, g = (t >> 6) & 3, m = t >> 8;
+    const int row = 16 * m + 4 * g + e;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sum += red[w][m][16 * g + c][e];
+    if (row < rows) Y[(int64_t)row * out + o0 + c] = bf16_t{f32_to_bf16(sum)};
+  }
+}
+
+template <int MT>
+void launch_skinny(const void *X, const void *W, int rows, int hidden, int out, void *Y, hipStream_t s) {
+  hipLaunchKernelGGL((project_skinny_kernel<MT>), dim3(out / 16), dim3(512), 0, s, static_cast<const bf16_t *>(X),
+                     static_cast<const bf16_t *>(W), rows, hidden, out, static_cast<bf16_t *>(Y));
+}
+
 }  // namespace
 
 hipError_t launch_project(const void *X, const void *W, int64_t rows, int hidden, int out, void *Y, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (rows <= SKINNY_ROWS) {
+    const int r = (int)rows;
+    if (r <= 16) launch_skinny<1>(X, W, r, hidden, out, Y, s);
+    else if (r <= 32) launch_skinny<2>(X, W, r, hidden, out, Y, s);
+    else if (r <= 48) launch_skinny<3>(X, W, r, hidden, out, Y, s);
+    else launch_skinny<4>(X, W, r, hidden, out, Y, s);
+    return hipGetLastError();
+  }
   const int n_rtiles = (int)((rows + PT - 1) / PT), n_otiles = out / PT;
   const int64_t grid = 8 * (int64_t)n_otiles * ((n_rtiles + 7) / 8);
   hipLaunchKernelGGL(project_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(X),

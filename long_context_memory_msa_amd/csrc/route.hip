@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
   // while the MFMAs of the current step run; it streams across tile ends.
   // Inverse norms and document ids of the next tile are fetched one tile ahead.
   constexpr int PD = HR < MSA_ROUTE_PD ? HR : MSA_ROUTE_PD;
+  static_assert(HR % PD == 0, "ring slots are reused across tiles: the depth must divide the head count");
   FT ring[PD][KS];
   float ik_cur[HR], ik_nxt[HR];
   int doc_cur = -1, doc_nxt = -1;
@@ -170,7 +171,8 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
 #pragma unroll
       for (int j = 0; j < HR; ++j) ik[j] = ip[j];
     }
-    doc = (tl * 16 + col < a.n_chunks) ? a.chunk_doc[cp] : -1;
+    const int d = a.chunk_doc[cp];  // unconditional load (cp is clamped)
+    doc = (tl * 16 + col < a.n_chunks) ? d : -1;
   };
 #if MSA_ROUTE_QREG
   FT qreg[NF];
@@ -194,11 +196,13 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
     const int64_t tile_next = tile + t_step;
     const int64_t c = tile * 16 + col;
     const bool cv = c < a.n_chunks;
-    const bool more = tile_next < t_hi;
-    if (more) {
-      kp_nxt = krbar + lane_chunk(tile_next) * (HR * DR) + G * EL;
-      load_meta(tile_next, ik_nxt, doc_nxt);
-    }
+    // The loads for the next tile are issued unconditionally (after the
+    // wave's last tile they re-read this tile and are never used): loads
+    // under a branch make the compiler's wait counts at the join assume the
+    // branch was not taken, which drains every load in flight once per tile.
+    const int64_t tile_pf = tile_next < t_hi ? tile_next : tile;
+    kp_nxt = krbar + lane_chunk(tile_pf) * (HR * DR) + G * EL;
+    load_meta(tile_pf, ik_nxt, doc_nxt);
 #if !MSA_ROUTE_QREG
     // opaque zero: keeps the query-fragment LDS reads inside the loop rather
     // than hoisting all of Q into VGPRs (registers go to the prefetch ring)
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
       if (h + PD < HR) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) ring[slot][s] = load_stream<T>(kp_cur + (h + PD) * DR + s * KW);
-      } else if (more) {
+      } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) ring[slot][s] = load_stream<T>(kp_nxt + (h + PD - HR) * DR + s * KW);
       }
