@@ -51,6 +51,10 @@
 #ifndef MSA_ROUTE_WAVES
 #define MSA_ROUTE_WAVES 3
 #endif
+// 1 = size the persistent grid so that every wave gets the same number of tiles
+#ifndef MSA_ROUTE_BALANCE
+#define MSA_ROUTE_BALANCE 1
+#endif
 
 namespace msa {
 namespace {
@@ -106,33 +110,6 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
   const int n_rows = a.n_q * a.t_r;
   const T *qr = static_cast<const T *>(a.qr);
 
-  // query fragments of rows [16 rb, 16 rb + 16) in MFMA A-operand order
-  for (int e = threadIdx.x; e < NF * 64; e += 256) {
-    const int f = e >> 6, l = e & 63, h = f / KS, s = f % KS;
-    const int row = rb * 16 + (l & 15);
-    if (row < n_rows) {
-      qfrag[f][l] = load_frag<T>(qr + ((int64_t)row * HR + h) * DR + s * KW + (l >> 4) * EL);
-    } else {
-      FT z;
-      if constexpr (EL == 1) z = 0.f; else z = FT{};
-      qfrag[f][l] = z;
-    }
-  }
-  if (threadIdx.x < 16 * HR) {
-    const int r = threadIdx.x & 15, h = threadIdx.x >> 4;
-    const int row = rb * 16 + r;
-    float ss = 0.f;
-    if (row < n_rows) {
-      const T *p = qr + ((int64_t)row * HR + h) * DR;
-      for (int i = 0; i < DR; ++i) {
-        float x = Elem<T>::to_f32(p[i]);
-        ss += x * x;
-      }
-    }
-    qinv[h][r] = ss > 0.f ? (1.0f / sqrtf(ss)) * (1.0f / HR) : 0.f;
-  }
-  __syncthreads();
-
   // rows of this lane: 16 rb + 4 G + i; a row block lies in one query when t_r % 16 == 0
   const bool uniform = (a.t_r % 16) == 0;
   int rowq[4];
@@ -174,6 +151,59 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
     const int d = a.chunk_doc[cp];  // unconditional load (cp is clamped)
     doc = (tl * 16 + col < a.n_chunks) ? d : -1;
   };
+  const T *kp_cur = krbar + lane_chunk(t_lo) * (HR * DR) + G * EL;
+  const T *kp_nxt = kp_cur;
+  // the key stream starts before the query staging below (unconditionally:
+  // a wave without tiles reads a clamped, valid chunk and never uses it)
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) ring[p][s] = load_stream<T>(kp_cur + p * DR + s * KW);
+  load_meta(t_lo, ik_cur, doc_cur);
+
+  // query fragments of rows [16 rb, 16 rb + 16) in MFMA A-operand order: all
+  // loads in flight together, then written to LDS
+  {
+    constexpr int QPT = (NF * 64 + 255) / 256;
+    FT qt[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      const int f = e >> 6, l = e & 63, h = f / KS, s = f % KS;
+      const int row = rb * 16 + (l & 15);
+      if constexpr (EL == 1) qt[i] = 0.f; else qt[i] = FT{};
+      if (e < NF * 64 && row < n_rows) qt[i] = load_frag<T>(qr + ((int64_t)row * HR + h) * DR + s * KW + (l >> 4) * EL);
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      if (e < NF * 64) qfrag[e >> 6][e & 63] = qt[i];
+    }
+  }
+  __syncthreads();
+  // (1/H_r) / ||Q^R[row, h]|| from the staged fragments (0 for a zero or absent row)
+  if (threadIdx.x < 16 * HR) {
+    const int r = threadIdx.x & 15, h = threadIdx.x >> 4;
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const FT v = qfrag[h * KS + s][16 * g + r];
+        if constexpr (EL == 1) {
+          ss += v * v;
+        } else {
+#pragma unroll
+          for (int j = 0; j < EL; ++j) {
+            const float x = (float)v[j];
+            ss += x * x;
+          }
+        }
+      }
+    qinv[h][r] = ss > 0.f ? (1.0f / sqrtf(ss)) * (1.0f / HR) : 0.f;
+  }
+  __syncthreads();
+
 #if MSA_ROUTE_QREG
   FT qreg[NF];
 #pragma unroll
@@ -182,15 +212,6 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
 #else
 #define MSA_QOP(f) qfrag[(f) + zoff][lane]
 #endif
-  const T *kp_cur = krbar + lane_chunk(t_lo) * (HR * DR) + G * EL;
-  const T *kp_nxt = kp_cur;
-  if (t_lo < t_hi) {
-#pragma unroll
-    for (int p = 0; p < PD; ++p)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) ring[p][s] = load_stream<T>(kp_cur + p * DR + s * KW);
-    load_meta(t_lo, ik_cur, doc_cur);
-  }
 
   for (int64_t tile = t_lo; tile < t_hi; tile += t_step) {
     const int64_t tile_next = tile + t_step;
@@ -336,6 +357,13 @@ hipError_t route_launch(const RouteArgs &a, hipStream_t s) {
   const int64_t slots = (int64_t)device_cu_count() * resident;  // resident workgroups
   int64_t wgs = std::max<int64_t>(1, slots / rbs);
   wgs = std::min<int64_t>(wgs, (n_tiles + 3) / 4);
+#if MSA_ROUTE_BALANCE
+  // Balance: as few waves as still need the same number of rounds, so that
+  // (nearly) every wave streams the same number of tiles and no small set of
+  // waves finishes a last, partial round alone at a fraction of the bandwidth.
+  const int64_t rounds = (n_tiles + 4 * wgs - 1) / (4 * wgs);
+  wgs = (n_tiles + 4 * rounds - 1) / (4 * rounds);
+#endif
   const int64_t n_waves = wgs * 4;  // wave w starts at tile w
   dim3 grid((unsigned)wgs, (unsigned)rbs), block(256);
   hipLaunchKernelGGL((route_scan_kernel<T, HR, DR, EDGE>), grid, block, 0, s, a, n_tiles, n_waves);
