@@ -1,15 +1,21 @@
-"""Decode steps of independent query batches with the attention of one step
-overlapping the routing of the next.
+"""Decode steps of independent query batches, the top-k and attention of one
+step overlapping the router scan of the next.
 
-The pages keep the pooled keys/values in host memory and load the selected
-documents' rows asynchronously, overlapped with the search (hotdry blog, key
-engineering details: tiered storage and asynchronous prefetch; wiselychen
-blog, mechanism 3).  With a tiered bank (``Bank(kv_host=True)``) the
-attention gathers those rows over the host link, a different resource from
-the HBM stream of the router scan, so the two can run at once on two streams:
+The router scan of a step streams the whole bank and is bound by HBM
+bandwidth; the top-k and the sparse attention after it are short,
+latency-bound kernels.  Independent query batches (other requests, other
+layers' queries) can therefore run their tail while the next batch is
+scanned, on two streams:
 
-  route stream:  [wait attend(s-2) done] route_score(s) -> topk(s) -> mark selected(s)
-  attend stream: [wait selected(s)] sparse_attend(s) -> mark done(s)
+  route stream: [wait tail(s-2) done] route_score(s) -> mark routed(s)
+  tail stream:  [wait routed(s)] topk(s) -> sparse_attend(s) -> mark done(s)
+
+The pages load the selected documents' pooled rows asynchronously while the
+search goes on (hotdry blog, key engineering details: tiered storage and
+asynchronous prefetch; wiselychen blog, mechanism 3); with a tiered bank
+(``Bank(kv_host=True)``) the attention's gather runs over the host link, a
+different resource from the scan's HBM stream, and the same two streams
+overlap it.
 
 Outputs are double-buffered by step parity: step s writes slot s % 2, which
 stays valid until step s + 2 is issued.  All computation runs in the library's
@@ -45,8 +51,8 @@ class DecodePipeline:
         self.val = [torch.empty((n_q, k), dtype=torch.float32, device=device) for _ in range(2)]
         self.O = [torch.empty((n_q, T, h_q, d), dtype=td, device=device) for _ in range(2)]
         self.route_stream = torch.cuda.Stream(device=device)
-        self.attend_stream = torch.cuda.Stream(device=device)
-        self.selected = [torch.cuda.Event() for _ in range(2)]
+        self.tail_stream = torch.cuda.Stream(device=device)
+        self.routed = [torch.cuda.Event() for _ in range(2)]
         self.done = [torch.cuda.Event() for _ in range(2)]
         self.issued = 0
 
@@ -55,21 +61,21 @@ class DecodePipeline:
         alive (and unchanged) until the step has run."""
         s = self.issued % 2
         c = self.bank.c
-        rs, at = self.route_stream, self.attend_stream
+        rs, ts = self.route_stream, self.tail_stream
         rs.wait_stream(torch.cuda.current_stream())  # the caller's inputs are ready
         if self.issued >= 2:
-            rs.wait_event(self.done[s])  # attend(step - 2) has read idx[s]
+            rs.wait_event(self.done[s])  # the tail of step - 2 has read s_doc[s]
         _lib.msa_route_score(c, QR, self.n_q, self.t_r, self.s_doc[s], None, self.ws_route, self.ws_route_n, rs)
+        self.routed[s].record(rs)
+        ts.wait_event(self.routed[s])
         _lib.msa_topk(self.s_doc[s], self.n_q, c.n_docs, self.k, self.idx[s], self.val[s], self.ws_topk,
-                      self.ws_topk_n, rs)
-        self.selected[s].record(rs)
-        at.wait_event(self.selected[s])
+                      self.ws_topk_n, ts)
         _lib.msa_sparse_attend(c, Q, K_loc, V_loc, self.n_q, self.T, self.L_loc, self.h_q, self.idx[s], self.k,
-                               self.pos0, self.scale, self.rope.c, self.O[s], self.ws_attend, self.ws_attend_n, at)
-        self.done[s].record(at)
+                               self.pos0, self.scale, self.rope.c, self.O[s], self.ws_attend, self.ws_attend_n, ts)
+        self.done[s].record(ts)
         self.issued += 1
         return s
 
     def synchronize(self) -> None:
         self.route_stream.synchronize()
-        self.attend_stream.synchronize()
+        self.tail_stream.synchronize()
