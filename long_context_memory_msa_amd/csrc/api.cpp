@@ -470,6 +470,7 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
       return stage_events ? hipEventRecord((hipEvent_t)stage_events[i], s) : hipSuccess;
     };
     hipError_t e = hipSuccess;
+    int n_fused = 0;  // > 0: the attention selects from this many candidates per query
     if (msa::route_single_writer(t_r)) {
       // scores written once per document: no zero fill, no keys
       float *scores = s_doc ? s_doc : reinterpret_cast<float *>(w);
@@ -492,7 +493,14 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
         src.mode = msa::TopkSrc::SCORES;
         if (e == hipSuccess) e = msa::launch_resolve_docs(ra, s);
       }
-      if (e == hipSuccess) e = msa::launch_topk(src, n_q, b->n_docs, k, idx, val, tk_ws, s);
+      // small k over a sliced bank: pass 1 here, the final selection of each
+      // query inside the attention workgroups (one kernel less)
+      n_fused = msa::topk_single_pass(b->n_docs) ? 0 : msa::topk_fused_candidates(b->n_docs, k);
+      if (n_fused > 0) {
+        if (e == hipSuccess) e = msa::launch_topk_pass1(src, n_q, b->n_docs, k, tk_ws, s);
+      } else {
+        if (e == hipSuccess) e = msa::launch_topk(src, n_q, b->n_docs, k, idx, val, tk_ws, s);
+      }
       if (e == hipSuccess) e = rec(2);
     } else {
       uint32_t *keys = reinterpret_cast<uint32_t *>(w);
@@ -512,8 +520,16 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
         if (e == hipSuccess) e = msa::launch_keys_to_scores(reinterpret_cast<uint32_t *>(s_doc), nd, s);
       }
     }
-    if (e == hipSuccess)
-      e = msa::launch_attend(attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, idx, k, pos0, scale, rope, O), at_ws, s);
+    if (e == hipSuccess) {
+      msa::AttendArgs aa = attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, idx, k, pos0, scale, rope, O);
+      if (n_fused > 0) {
+        aa.cand = static_cast<const uint64_t *>(tk_ws);
+        aa.n_cand = n_fused;
+        aa.idx_out = idx;
+        aa.val_out = val;
+      }
+      e = msa::launch_attend(aa, at_ws, s);
+    }
     if (e == hipSuccess) e = rec(3);
     return e == hipSuccess ? ok() : dev_fail(e, "layer_forward");
   } catch (...) {

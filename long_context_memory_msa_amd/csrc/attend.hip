@@ -22,6 +22,7 @@
 
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
+#include "select_wave.hpp"
 
 namespace msa {
 namespace {
@@ -64,6 +65,8 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   __shared__ __align__(16) T sV[D * VROW];
   __shared__ int32_t sP[MAX_K + 1];   // prefix of selected documents' chunk counts
   __shared__ int64_t sCB[MAX_K];      // first chunk of each selected document
+  __shared__ __align__(16) uint32_t sHist[256];  // in-kernel selection: radix histogram
+  __shared__ uint64_t sSel[128];                 // and the compacted / ranked winners
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, G = lane >> 4;
@@ -129,12 +132,27 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
 
   // selected documents -> chunk prefix
   if (threadIdx.x < 64) {
+    // in-kernel selection: rank-r document of this query in lane r (k <= 64)
+    int sel_doc = 0;
+    if (a.cand) {
+      constexpr int CI = ATTEND_MAX_CAND / 64;
+      const uint64_t *cq = a.cand + (int64_t)q * a.n_cand;
+      uint64_t v[CI];
+#pragma unroll
+      for (int j = 0; j < CI; ++j) v[j] = j * 64 + lane < a.n_cand ? cq[j * 64 + lane] : 0;
+      const uint64_t e = wave_topk_sorted<CI>(v, (uint32_t)a.k, sHist, sSel);
+      sel_doc = (int)(0xFFFFFFFFu - (uint32_t)e);
+      if (a.idx_out && kvh == 0 && split == 0 && rbg == 0 && lane < a.k) {
+        a.idx_out[(int64_t)q * a.k + lane] = sel_doc;
+        a.val_out[(int64_t)q * a.k + lane] = key_score((uint32_t)(e >> 32));
+      }
+    }
     int carry = 0;
     for (int base = 0; base < a.k; base += 64) {
       const int r = base + lane;
       int cnt = 0;
       if (r < a.k) {
-        int doc = a.idx[(int64_t)q * a.k + r];
+        int doc = a.cand ? sel_doc : a.idx[(int64_t)q * a.k + r];
         doc = doc < 0 ? 0 : (doc >= a.n_docs ? a.n_docs - 1 : doc);
         const int64_t c0 = a.doc_chunk_off[doc];
         cnt = (int)(a.doc_chunk_off[doc + 1] - c0);

@@ -103,6 +103,11 @@ struct TopkSrc {
 };
 hipError_t launch_topk(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,
                        hipStream_t s);
+// Pass 1 alone (the per-slice candidates, ws as for launch_topk) when the
+// final selection can be left to the attention kernel: returns the number of
+// candidates per query, or 0 when this top-k does not take that form.
+int topk_fused_candidates(int n_docs, int k);
+hipError_t launch_topk_pass1(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s);
 
 // ---- router projection -------------------------------------------------------
 // Y[rows][out] = X[rows][hidden] W[out][hidden]^T, bf16 in and out, fp32 accumulation;
@@ -126,7 +131,17 @@ struct AttendArgs {
   const float *cos, *sin;
   void *O;
   int max_doc_chunks;
+  // In-kernel selection (optional): when cand is set, the documents are the
+  // top-k of the query's n_cand pass-1 candidates (composites, 0 = empty),
+  // taken by each workgroup itself instead of read from idx; the workgroups
+  // of KV head 0, split 0, row group 0 write them to idx_out / val_out.
+  const uint64_t *cand = nullptr;
+  int n_cand = 0;
+  int32_t *idx_out = nullptr;
+  float *val_out = nullptr;
 };
+// candidates per query an attention workgroup can select from (16 per lane)
+constexpr int ATTEND_MAX_CAND = 1024;
 int attend_splits(const AttendArgs &a);
 size_t attend_ws_bytes(const AttendArgs &a);
 hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s);

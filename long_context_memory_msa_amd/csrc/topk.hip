@@ -24,6 +24,7 @@
 
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
+#include "select_wave.hpp"
 
 namespace msa {
 namespace {
@@ -44,30 +45,6 @@ struct SelShared {
 #ifndef MSA_TOPK_SINGLE_MAX
 #define MSA_TOPK_SINGLE_MAX 8192
 #endif
-
-// Histogram add for a digit that most lanes share (the first, sign/exponent
-// digit of cosine scores): the two digits met first in the wave are added with
-// one LDS atomic each, the remaining lanes add one by one.  (An exhaustive
-// loop over distinct digits costs one shuffle round trip per digit; scores
-// spread over several binades made it slower than plain atomics.)  Every lane
-// of the wave must call it.
-__device__ __forceinline__ void hist_add_wave(uint32_t *hist, uint32_t digit, bool active) {
-  unsigned long long pending = __ballot(active);
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    if (!pending) break;
-    const int leader = __ffsll((long long)pending) - 1;
-    const uint32_t d = __shfl(digit, leader, 64);
-    const unsigned long long same = __ballot(active && digit == d);
-    if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[d], (uint32_t)__popcll(same));
-    pending &= ~same;
-  }
-  if ((pending >> (threadIdx.x & 63)) & 1ull) atomicAdd(&hist[digit], 1u);
-}
-
-__device__ __forceinline__ uint64_t composite(uint32_t key, int64_t i) {
-  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-}
 
 // Exclusive prefix sum over the block; returns this thread's offset, *total.
 __device__ int block_excl_scan(int v, SelShared &sh, int *total) {
@@ -361,73 +338,6 @@ constexpr int WS_SLICE = 512;
 constexpr int WS_ITEMS = WS_SLICE / 64;
 constexpr int WS_MAX_K = 32;  // k up to this uses the wave pass (k <= slice / 16)
 
-// orders this wave's LDS accesses before and after it (LDS executes a wave's
-// operations in order; this keeps the compiler from moving them across)
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int ITEMS>
-__device__ void select_wave(const uint64_t (&v)[ITEMS], uint32_t need, uint32_t *hist, int *out_shift,
-                            uint64_t *out_prefix) {
-  const int lane = threadIdx.x & 63;
-  uint64_t prefix = 0;
-  int shift = 56;
-  for (;; shift -= 8) {
-    reinterpret_cast<uint4 *>(hist)[lane] = uint4{0u, 0u, 0u, 0u};
-    wave_sync();
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-      const bool match = v[j] != 0 && ((shift == 56) || ((v[j] ^ prefix) >> (shift + 8)) == 0);
-      const uint32_t digit = (uint32_t)(v[j] >> shift) & 255;
-      if (shift == 56) hist_add_wave(hist, digit, match);
-      else if (match) atomicAdd(&hist[digit], 1u);
-    }
-    wave_sync();
-    // lane l owns bins 255-4l .. 252-4l (descending digit order)
-    uint32_t c[4], sum = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[j] = hist[255 - 4 * lane - j];
-      sum += c[j];
-    }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    const unsigned long long m = __ballot(incl >= need);
-    const int first = __ffsll((long long)m) - 1;
-    uint32_t bin = 0, above = 0, in_bin = 0;
-    {
-      uint32_t cum = incl - sum;
-      bool found = false;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (!found && cum + c[j] >= need) {
-          bin = 255 - 4 * lane - j;
-          above = cum;
-          in_bin = c[j];
-          found = true;
-        }
-        cum += c[j];
-      }
-    }
-    bin = __shfl(bin, first, 64);
-    above = __shfl(above, first, 64);
-    in_bin = __shfl(in_bin, first, 64);
-    wave_sync();  // the histogram is read before the next pass clears it
-    prefix |= (uint64_t)bin << shift;
-    need -= above;
-    if (in_bin == need || shift == 0) break;
-  }
-  *out_shift = shift;
-  *out_prefix = prefix;
-}
-
 template <int MODE>
 __global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, int k, int n_slices,
                                                         uint64_t *cand) {
@@ -591,6 +501,36 @@ hipError_t topk_launch(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *
     hipLaunchKernelGGL(topk_pass2_regs, dim3(n_q), dim3(P2_THREADS), 0, s, cand, (int)n_cand, k, kpad, idx, val);
   else
     hipLaunchKernelGGL(topk_pass2, dim3(n_q), dim3(TK_THREADS), 0, s, cand, n_cand, k, kpad, idx, val);
+  return hipGetLastError();
+}
+
+// 1 = the layer leaves the final selection to the attention kernel where it can
+#ifndef MSA_TOPK_FUSE
+#define MSA_TOPK_FUSE 1
+#endif
+
+int topk_fused_candidates(int n_docs, int k) {
+  if (!MSA_TOPK_FUSE || topk_single_pass(n_docs) || slice_for(k) != WS_SLICE) return 0;
+  const int64_t n = (int64_t)n_slices_for(n_docs, k) * k;
+  return n <= ATTEND_MAX_CAND ? (int)n : 0;
+}
+
+hipError_t launch_topk_pass1(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s) {
+  const int ns = n_slices_for(n_docs, k);
+  uint64_t *cand = static_cast<uint64_t *>(ws);
+  switch (src.mode) {
+    case TopkSrc::SCORES:
+      hipLaunchKernelGGL(topk_pass1_wave<TopkSrc::SCORES>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k,
+                         ns, cand);
+      break;
+    case TopkSrc::KEYS:
+      hipLaunchKernelGGL(topk_pass1_wave<TopkSrc::KEYS>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k, ns,
+                         cand);
+      break;
+    default:
+      hipLaunchKernelGGL(topk_pass1_wave<TopkSrc::EDGES>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k,
+                         ns, cand);
+  }
   return hipGetLastError();
 }
 
