@@ -79,6 +79,29 @@ def route_traffic(bytes_per_launch: int):
         return None
 
 
+def run_pipelined(bank, rope, w, scale, dev, QR, Q, Kl, Vl, idx, O_, args) -> float:
+    """Wall time of --steps independent decode steps through the two-stream
+    pipeline; the last step's output must equal msa_layer_forward's."""
+    import torch
+
+    from long_context_memory_msa_amd.pipeline import DecodePipeline
+
+    pipe = DecodePipeline(bank, rope, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, scale, dev)
+    for _ in range(args.warmup):
+        pipe.step(QR, Q, Kl, Vl)
+    pipe.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        last = pipe.step(QR, Q, Kl, Vl)
+    pipe.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if not (torch.equal(pipe.idx[last], idx) and torch.equal(pipe.O[last], O_)):
+        raise RuntimeError("pipelined step differs from msa_layer_forward")
+    return wall
+
+
 def cpu_baseline(w, qi, n_docs: int) -> dict:
     """The fp64 oracle's layer forward on the first ``n_docs`` documents of the
     bank (pooled-shape synthetic values; the oracle's time does not depend on
@@ -431,6 +454,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sequential-only", action="store_true",
+                    help="decode: time only the sequential msa_layer_forward steps (for kernel profiles)")
     ap.add_argument("--cpu-docs", type=int, default=-1,
                     help="oracle baseline sample: first N documents (-1 = the whole bank, 0 = skip)")
     ap.add_argument("--bank-tokens", type=int, default=None, help="smaller bank for a quick look (not the metric)")
@@ -536,21 +561,11 @@ def main() -> int:
     ms_seq = wall / args.steps * 1e3
 
     # pipelined steps: the same batch issued as independent steps, two in flight
-    from long_context_memory_msa_amd.pipeline import DecodePipeline
-    pipe = DecodePipeline(bank, rope, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, scale, dev)
-    for _ in range(args.warmup):
-        pipe.step(QR, Q, Kl, Vl)
-    pipe.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        last = pipe.step(QR, Q, Kl, Vl)
-    pipe.synchronize()
-    torch.cuda.synchronize()
-    wall_p = time.perf_counter() - t0
-    if not (torch.equal(pipe.idx[last], idx) and torch.equal(pipe.O[last], O_)):
-        raise RuntimeError("pipelined step differs from msa_layer_forward")
-
+    # (--sequential-only: skipped, value from the sequential steps; for profiles)
+    if args.sequential_only:
+        wall_p = wall
+    else:
+        wall_p = run_pipelined(bank, rope, w, scale, dev, QR, Q, Kl, Vl, idx, O_, args)
     ms_step = wall_p / args.steps * 1e3
     route_ms = statistics.mean(route)
     scan_bytes = w.n_chunks * (w.h_r * w.d_r * esz + 4 * w.h_r + 4)   # K^R rows + inverse norms + chunk->doc
@@ -572,7 +587,8 @@ def main() -> int:
                                 "docs U[512,8192], chunk 128, 8 router heads x 128, 32 q / 8 KV heads x 128"),
                    "bank_tokens": w.n_tok, "n_docs": w.n_docs, "n_chunks": w.n_chunks, "queries": w.n_q,
                    "query_tokens": w.T, "k": w.k, "chunk": w.chunk},
-        "pipelined": {"streams": 2, "overlap": "top-k + attention of step s during the router scan of step s+1"},
+        "pipelined": (None if args.sequential_only else
+                      {"streams": 2, "overlap": "top-k + attention of step s during the router scan of step s+1"}),
         "sequential": {"ms_per_step": ms_seq, "value": w.n_tok / (ms_seq * 1e-3)},
         "layer_latency_ms": statistics.median(layer),
         "stage_ms": {"route": statistics.median(route), "topk": statistics.median(topk),

@@ -221,8 +221,11 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
     // wave's last tile they re-read this tile and are never used): loads
     // under a branch make the compiler's wait counts at the join assume the
     // branch was not taken, which drains every load in flight once per tile.
-    const int64_t tile_pf = tile_next < t_hi ? tile_next : tile;
-    kp_nxt = krbar + lane_chunk(tile_pf) * (HR * DR) + G * EL;
+    const bool has_next = tile_next < t_hi;
+    const int64_t tile_pf = has_next ? tile_next : tile;
+    // (the last tile's stand-in loads read its own final PD heads, fetched
+    // moments earlier, so they are served by L2 rather than HBM)
+    kp_nxt = krbar + lane_chunk(tile_pf) * (HR * DR) + G * EL + (has_next ? 0 : (HR - PD) * DR);
     load_meta(tile_pf, ik_nxt, doc_nxt);
 #if !MSA_ROUTE_QREG
     // opaque zero: keeps the query-fragment LDS reads inside the loop rather
