@@ -79,6 +79,30 @@ def route_traffic(bytes_per_launch: int):
         return None
 
 
+def pct(xs) -> list:
+    """p10, p50, p90 of a list of times."""
+    ys = sorted(xs)
+    return [ys[int(round(f * (len(ys) - 1)))] for f in (0.1, 0.5, 0.9)]
+
+
+def attend_roofline(w, bank, gi, attend_ms: float) -> dict:
+    """Attention stage against both rooflines: algorithmic FLOPs
+    4 * H_q * d * sum over rows of the visible keys (selected documents' pooled
+    rows + causal local keys) over the bf16 MFMA peak, and the gathered pooled
+    K/V rows + Q, local K/V and O bytes over the HBM peak."""
+    off = bank.doc_chunk_off_host
+    n_mem = [sum(int(off[d + 1] - off[d]) for d in gi[q]) for q in range(w.n_q)]
+    vis = sum(n_mem[q] + (w.L_loc - w.T + t + 1) for q in range(w.n_q) for t in range(w.T))
+    flop = 4.0 * w.h_q * w.d * vis
+    esz = 2 if w.dtype == "bf16" else 4
+    nbytes = (sum(n_mem) * w.h_kv * w.d * 2 + w.n_q * w.T * w.h_q * w.d * 2
+              + w.n_q * w.L_loc * w.h_kv * w.d * 2) * esz
+    sec = attend_ms * 1e-3
+    return {"flop": flop, "bytes": nbytes, "TFLOP/s": flop / sec / 1e12, "mfma_frac": flop / sec / 2.5e15,
+            "GB/s": nbytes / sec / 1e9, "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+            "note": "stage time includes the in-kernel top-k selection and the split merge"}
+
+
 def run_pipelined(bank, rope, w, scale, dev, QR, Q, Kl, Vl, idx, O_, args) -> float:
     """Wall time of --steps independent decode steps through the two-stream
     pipeline; the last step's output must equal msa_layer_forward's."""
@@ -593,6 +617,9 @@ def main() -> int:
         "layer_latency_ms": statistics.median(layer),
         "stage_ms": {"route": statistics.median(route), "topk": statistics.median(topk),
                      "attend": statistics.median(attend)},
+        "route_ms_p10_p50_p90": pct(route),
+        "layer_ms_p10_p50_p90": pct(layer),
+        "attend_roofline": attend_roofline(w, bank, gi, statistics.median(attend)),
         "route_tokens_per_s": w.n_tok / (route_ms * 1e-3),
         "roofline": {"bound": "hbm", "kernel": "route_scan", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": route_traffic(scan_bytes),

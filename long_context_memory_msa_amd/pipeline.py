@@ -17,9 +17,14 @@ asynchronous prefetch; wiselychen blog, mechanism 3); with a tiered bank
 different resource from the scan's HBM stream, and the same two streams
 overlap it.
 
-Outputs are double-buffered by step parity: step s writes slot s % 2, which
-stays valid until step s + 2 is issued.  All computation runs in the library's
-kernels; this module only orders launches on streams.
+Outputs rotate over `slots` buffers: step s writes slot s % slots, which
+stays valid until step s + slots is issued.  The route stream never waits on
+the GPU: before reusing a slot the host waits for the tail that last read it
+(long finished when the slots outnumber the steps in flight), and the
+caller's stream is waited on only while it still has work queued (a
+cross-stream wait on the route stream delayed each scan by 10-20 us).  All
+computation runs in the library's kernels; this module only orders launches
+on streams.
 """
 from __future__ import annotations
 
@@ -33,7 +38,7 @@ from .memory import TORCH_DTYPE, Bank, Rope, workspace
 
 class DecodePipeline:
     def __init__(self, bank: Bank, rope: Rope, n_q: int, T: int, t_r: int, L_loc: int, h_q: int, k: int, pos0: int,
-                 scale: Optional[float] = None, device="cuda"):
+                 scale: Optional[float] = None, device="cuda", slots: int = 4):
         self.bank, self.rope = bank, rope
         self.n_q, self.T, self.t_r, self.L_loc, self.h_q, self.k, self.pos0 = n_q, T, t_r, L_loc, h_q, k, pos0
         d = bank.c.d
@@ -46,25 +51,28 @@ class DecodePipeline:
         self.ws_topk = workspace(self.ws_topk_n, device)
         self.ws_attend = workspace(self.ws_attend_n, device)
         td = TORCH_DTYPE[bank.dtype]
-        self.s_doc = [torch.empty((n_q, c.n_docs), dtype=torch.float32, device=device) for _ in range(2)]
-        self.idx = [torch.empty((n_q, k), dtype=torch.int32, device=device) for _ in range(2)]
-        self.val = [torch.empty((n_q, k), dtype=torch.float32, device=device) for _ in range(2)]
-        self.O = [torch.empty((n_q, T, h_q, d), dtype=td, device=device) for _ in range(2)]
+        self.s_doc = [torch.empty((n_q, c.n_docs), dtype=torch.float32, device=device) for _ in range(slots)]
+        self.idx = [torch.empty((n_q, k), dtype=torch.int32, device=device) for _ in range(slots)]
+        self.val = [torch.empty((n_q, k), dtype=torch.float32, device=device) for _ in range(slots)]
+        self.O = [torch.empty((n_q, T, h_q, d), dtype=td, device=device) for _ in range(slots)]
         self.route_stream = torch.cuda.Stream(device=device)
         self.tail_stream = torch.cuda.Stream(device=device)
-        self.routed = [torch.cuda.Event() for _ in range(2)]
-        self.done = [torch.cuda.Event() for _ in range(2)]
+        self.routed = [torch.cuda.Event() for _ in range(slots)]
+        self.done = [torch.cuda.Event() for _ in range(slots)]
+        self.slots = slots
         self.issued = 0
 
     def step(self, QR, Q, K_loc, V_loc) -> int:
         """Issue one decode step; returns its output slot.  The inputs must stay
         alive (and unchanged) until the step has run."""
-        s = self.issued % 2
+        s = self.issued % self.slots
         c = self.bank.c
         rs, ts = self.route_stream, self.tail_stream
-        rs.wait_stream(torch.cuda.current_stream())  # the caller's inputs are ready
-        if self.issued >= 2:
-            rs.wait_event(self.done[s])  # the tail of step - 2 has read s_doc[s]
+        if self.issued >= self.slots:
+            self.done[s].synchronize()  # the tail of step - slots has read s_doc[s] and written idx/O[s]
+        cur = torch.cuda.current_stream()
+        if not cur.query():
+            rs.wait_stream(cur)  # the caller's inputs are still being produced
         _lib.msa_route_score(c, QR, self.n_q, self.t_r, self.s_doc[s], None, self.ws_route, self.ws_route_n, rs)
         self.routed[s].record(rs)
         ts.wait_event(self.routed[s])

@@ -76,7 +76,8 @@ def test_decode_pipeline_equals_layer_forward(device, kv_host):
     ref, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
     bank = _tiered_bank(w, K, V, KR, rope, device) if kv_host else ref
     batches = [query_views(w, W.query_inputs(w, layer), device) for layer in range(4)]
-    pipe = DecodePipeline(bank, rope, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, device=device)
+    # two slots: the second pair reuses the first pair's buffers (host-side wait)
+    pipe = DecodePipeline(bank, rope, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, device=device, slots=2)
     for pair in ((0, 1), (2, 3)):
         slots = [pipe.step(*batches[i]) for i in pair]
         pipe.synchronize()
