@@ -348,6 +348,50 @@ def test_layer_equals_composition_and_is_deterministic(device):
     assert torch.equal(s_doc, s1) and torch.equal(idx, i1) and torch.equal(val, v1) and torch.equal(out, o1)
 
 
+@pytest.mark.parametrize("k", [16, 32])
+def test_layer_sliced_topk_selected_in_attention(device, k):
+    # more documents than one top-k workgroup holds (8,192), small k: the layer
+    # runs top-k pass 1 only and every attention workgroup selects its
+    # query's documents from the candidates itself; it must equal the
+    # separate route / top-k / attend calls bit for bit, and the oracle
+    g = np.random.default_rng(11)
+    lens = g.integers(8, 41, size=9_000).astype(np.int64)  # one chunk per document
+    w = _wl(3, 200_000, doc_lens=lens, chunk=64, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, n_q=4, k=k, pos0=k,
+            gold=np.zeros((4, 0), dtype=np.int64))
+    assert w.n_docs > 8192 and w.n_chunks == w.n_docs
+    log(f"sliced layer k={k}: docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
+    QR, Q, Kl, Vl = query_views(w, qi, device)
+    o1, i1, v1, s1 = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+    s_doc = torch.empty_like(s1)
+    nb0 = L.msa_route_workspace_bytes(bank.c, w.n_q, w.T_route)
+    L.msa_route_score(bank.c, QR, w.n_q, w.T_route, s_doc, None, M.workspace(nb0, device), nb0)
+    idx, val = torch.empty_like(i1), torch.empty_like(v1)
+    nb = L.msa_topk_workspace_bytes(w.n_q, w.n_docs, w.k)
+    L.msa_topk(s_doc, w.n_q, w.n_docs, w.k, idx, val, M.workspace(nb, device), nb)
+    out = torch.empty_like(o1)
+    nb2 = L.msa_attend_workspace_bytes(bank.c, w.n_q, w.T, w.L_loc, w.h_q, w.k)
+    L.msa_sparse_attend(bank.c, Q, Kl, Vl, w.n_q, w.T, w.L_loc, w.h_q, idx, w.k, w.pos0, L.default_scale(w.d),
+                        rope.c, out, M.workspace(nb2, device), nb2)
+    torch.cuda.synchronize()
+    assert torch.equal(s_doc, s1) and torch.equal(idx, i1) and torch.equal(val, v1) and torch.equal(out, o1)
+    want = O.layer_forward(qi["QR"][:, w.L_loc - w.T_route:w.L_loc], qi["Q"][:, w.L_loc - w.T:w.L_loc],
+                           qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], ob, w.k, w.pos0, base=w.rope_base)
+    assert np.abs(host(s1) - want["s_doc"]).max() <= 2e-3
+    gi = i1.cpu().numpy()
+    same = True
+    for q in range(w.n_q):
+        if want["gap"][q] > 4e-3:
+            assert set(gi[q].tolist()) == set(want["idx"][q].tolist())
+        same &= set(gi[q].tolist()) == set(want["idx"][q].tolist())
+    topk_set_valid(gi, want["s_doc"], w.k)
+    o_ref = O.attend(qi["Q"][:, w.L_loc - w.T:w.L_loc], qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc],
+                     ob["kbar"], ob["vbar"], ob["doc_chunk_off"], gi, w.pos0, base=w.rope_base)
+    assert_attention_close(host(o1), o_ref)
+
+
 def test_interleave_small(device):
     # the interleave driver on 2 layers of a small bank against the oracle's loop
     from long_context_memory_msa_amd.interleave import interleave
