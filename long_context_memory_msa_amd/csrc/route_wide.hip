@@ -19,8 +19,9 @@
 //    a head's slices sit at one offset inside every 2 KB key row, and
 //    concurrent tiles on different heads spread the reads over the L2
 //    channels;
-//  * the K loop runs in stages of half a head; the next stage's slices are
-//    loaded into registers while the current one is multiplied;
+//  * the K loop runs in stages of half a head, filled by direct-to-LDS loads
+//    into XOR-swizzled 128-byte rows, double-buffered: the next stage fills
+//    while the current one is multiplied;
 //  * all row tiles of one chunk tile are scheduled on the same XCD
 //    (blockIdx % 8), so the chunk tile is read from HBM once and re-read from
 //    that XCD's L2;
