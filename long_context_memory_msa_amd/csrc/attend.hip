@@ -15,7 +15,9 @@
 //    each lane's probabilities are already the B operand of O^T = V^T P^T;
 //  * K/V tiles of 32 keys are gathered into LDS by the workgroup: pooled rows
 //    of the selected documents' chunks in rank order, then local keys rotated
-//    at pos0 + s on the fly; V is stored transposed for the PV operand;
+//    at pos0 + s on the fly; bf16 V rows are stored as they are and read
+//    transposed by ds_read_b64_tr_b16 (gfx950) into the V^T operand, fp32 V
+//    is stored transposed;
 //  * the key list is split across workgroups when there are few rows
 //    (decode); partial (max, sum, O) triples are merged by a log-sum-exp pass.
 #include <algorithm>
@@ -44,6 +46,17 @@ template <typename T> struct VPack;
 template <> struct VPack<float> { static constexpr int PAD = 4; };
 template <> struct VPack<bf16_t> { static constexpr int PAD = 8; };
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16: 8 bytes per lane, 16-bit elements transposed within
+// each group of 16 lanes (gfx950)
+template <typename T>
+__device__ __forceinline__ v4i16 lds_read_tr16(const T *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16 *)(reinterpret_cast<uintptr_t>(p)));
+}
+
 struct SplitOut {
   float *o;  // [rows][n_split][d]
   float *m;  // [rows][n_split]
@@ -58,11 +71,12 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   constexpr int EPS = 16 / sizeof(T);                 // elements per 16-byte segment
   constexpr int NP = D / (2 * EPS);                   // segment pairs (x, x + D/2) per key row
   constexpr int KROW = D + VPack<T>::PAD;             // LDS row pitch of K (elements)
-  constexpr int VROW = KT + VPack<T>::PAD;            // LDS row pitch of V^T (elements)
+  constexpr bool VTR = sizeof(T) == 2;                // bf16: V row-major, transposed on read
+  constexpr int VROW = VTR ? KROW : KT + VPack<T>::PAD;  // pitch of V rows (bf16) / of V^T rows (fp32)
   constexpr int NT = 64 * WGW;
 
   __shared__ __align__(16) T sK[KT * KROW];
-  __shared__ __align__(16) T sV[D * VROW];
+  __shared__ __align__(16) T sV[VTR ? KT * VROW : D * VROW];
   __shared__ int32_t sP[MAX_K + 1];   // prefix of selected documents' chunk counts
   __shared__ int64_t sCB[MAX_K];      // first chunk of each selected document
   __shared__ __align__(16) uint32_t sHist[256];  // in-kernel selection: radix histogram
@@ -243,22 +257,13 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       if (u >= KT * NP) continue;
       const int key = u / NP, m = u % NP;
       if constexpr (sizeof(T) == 2) {
+        // bf16 V rows (pooled or local: no rotation) go to LDS as they are
+        *reinterpret_cast<uint4 *>(sV + key * VROW + m * EPS) = rv[i][0];
+        *reinterpret_cast<uint4 *>(sV + key * VROW + D / 2 + m * EPS) = rv[i][1];
         if (rpos[i] < 0) {
-          // pooled (or zero) bf16 key: the words go to LDS as they are; V^T
-          // takes each 16-bit element straight from its word
+          // pooled (or zero) bf16 key: the words go to LDS as they are
           *reinterpret_cast<uint4 *>(sK + key * KROW + m * EPS) = rk[i][0];
           *reinterpret_cast<uint4 *>(sK + key * KROW + D / 2 + m * EPS) = rk[i][1];
-          uint16_t *v16 = reinterpret_cast<uint16_t *>(sV);
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const uint32_t wv[4] = {rv[i][p].x, rv[i][p].y, rv[i][p].z, rv[i][p].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int dim = p * (D / 2) + m * EPS + 2 * e;
-              v16[dim * VROW + key] = (uint16_t)(wv[e] & 0xFFFFu);
-              v16[(dim + 1) * VROW + key] = (uint16_t)(wv[e] >> 16);
-            }
-          }
           continue;
         }
       }
@@ -294,8 +299,10 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       for (int e = 0; e < EPS; ++e) {
         dK[e] = Elem<T>::from_f32(lo[e]);
         dK[D / 2 + e] = Elem<T>::from_f32(hi[e]);
-        sV[(m * EPS + e) * VROW + key] = Elem<T>::from_f32(vlo[e]);
-        sV[(D / 2 + m * EPS + e) * VROW + key] = Elem<T>::from_f32(vhi[e]);
+        if constexpr (!VTR) {
+          sV[(m * EPS + e) * VROW + key] = Elem<T>::from_f32(vlo[e]);
+          sV[(D / 2 + m * EPS + e) * VROW + key] = Elem<T>::from_f32(vhi[e]);
+        }
       }
     }
   };
@@ -365,12 +372,17 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
         w[2] = (uint32_t)f32_to_bf16(p[1][0]) | ((uint32_t)f32_to_bf16(p[1][1]) << 16);
         w[3] = (uint32_t)f32_to_bf16(p[1][2]) | ((uint32_t)f32_to_bf16(p[1][3]) << 16);
         const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
+        // V^T operand of lane (col, G): dims 16 mb + col, keys 4G..4G+3 and
+        // 16+4G..16+4G+3.  ds_read_b64_tr_b16 hands lane i of a 16-lane group
+        // element j of the 4 x 16 block that lanes 4j + i/4 address (8 bytes
+        // each), so lane a of the group addresses key 4G + a/4, dims
+        // 16 mb + 4 (a % 4) .. +3 of the row-major V tile.
+        const T *vb = sV + (4 * G + col / 4) * VROW + 4 * (col % 4);
 #pragma unroll
         for (int mb = 0; mb < D / 16; ++mb) {
-          const T *vr = sV + (16 * mb + col) * VROW;
-          const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + 4 * G);
-          const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 16 + 4 * G);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{v0.x, v0.y, v1.x, v1.y});
+          const v4i16 v0 = lds_read_tr16(vb + 16 * mb);
+          const v4i16 v1 = lds_read_tr16(vb + 16 * VROW + 16 * mb);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
           acc_o[mb] = mfma16(vf, pf, acc_o[mb]);
         }
       }
