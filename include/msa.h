@@ -269,6 +269,28 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
                       float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
                       size_t ws_bytes, void *const *stage_events, void *stream);
 
+/*
+ * The two halves of msa_layer_forward, for callers that overlap independent
+ * batches (the router scan of one batch streams the bank while the top-k and
+ * attention of the previous one run on another stream -- the pages overlap
+ * the loading of the selected documents with the search, [HD] key
+ * engineering details).  msa_layer_route runs the router scan into the layer
+ * workspace (and into s_doc, when given); msa_layer_select_attend then
+ * completes the document scores, selects the top-k and attends.  Called in
+ * this order on one workspace, with the same sizes and the same s_doc (or
+ * NULL both times), they enqueue exactly the kernels of msa_layer_forward:
+ * the outputs are identical.  The two calls may use different streams; the
+ * caller orders the second after the first (e.g. with an event) and keeps the
+ * workspace and s_doc untouched in between.  Workspace:
+ * msa_layer_workspace_bytes.  Errors: as msa_layer_forward.
+ */
+int msa_layer_route(const msa_bank *b, const void *QR, int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc,
+                    int32_t h_q, int32_t k, float *s_doc, void *ws, size_t ws_bytes, void *stream);
+int msa_layer_select_attend(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, int32_t n_q,
+                            int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0, float scale,
+                            const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
+                            size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

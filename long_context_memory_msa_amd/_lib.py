@@ -77,6 +77,9 @@ def _load():
         "msa_layer_workspace_bytes": ([bank_p, I32, I32, I32, I32, I32, I32], SZ),
         "msa_layer_forward": ([bank_p, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, rope_p, P, P, P, P, P, SZ,
                                P, P], ctypes.c_int),
+        "msa_layer_route": ([bank_p, P, I32, I32, I32, I32, I32, I32, P, P, SZ, P], ctypes.c_int),
+        "msa_layer_select_attend": ([bank_p, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, rope_p, P, P, P, P, P, SZ,
+                                     P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -197,6 +200,20 @@ def msa_layer_forward(bank: MsaBank, Q, K_loc, V_loc, QR, n_q: int, T: int, t_r:
     _check(_lib.msa_layer_forward(ctypes.byref(bank), _ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(QR), n_q, T, t_r,
                                   L_loc, h_q, k, pos0, scale, ctypes.byref(rope), _ptr(O), _ptr(idx), _ptr(val),
                                   _ptr(s_doc), _ptr(ws), ws_bytes, ev, _stream(stream)))
+
+
+def msa_layer_route(bank: MsaBank, QR, n_q: int, T: int, t_r: int, L_loc: int, h_q: int, k: int, s_doc, ws,
+                    ws_bytes: int, stream=None) -> None:
+    _check(_lib.msa_layer_route(ctypes.byref(bank), _ptr(QR), n_q, T, t_r, L_loc, h_q, k, _ptr(s_doc), _ptr(ws),
+                                ws_bytes, _stream(stream)))
+
+
+def msa_layer_select_attend(bank: MsaBank, Q, K_loc, V_loc, n_q: int, T: int, t_r: int, L_loc: int, h_q: int, k: int,
+                            pos0: int, scale: float, rope: MsaRope, O, idx, val, s_doc, ws, ws_bytes: int,
+                            stream=None) -> None:
+    _check(_lib.msa_layer_select_attend(ctypes.byref(bank), _ptr(Q), _ptr(K_loc), _ptr(V_loc), n_q, T, t_r, L_loc,
+                                        h_q, k, pos0, scale, ctypes.byref(rope), _ptr(O), _ptr(idx), _ptr(val),
+                                        _ptr(s_doc), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def default_scale(d: int) -> float:

@@ -201,6 +201,145 @@ int device_cu_count() {
 }
 }  // namespace msa
 
+namespace {
+
+// Validation shared by the layer entry points.  need_qr = false for the
+// second half, which does not read QR; the workspace layout depends on every
+// size.
+int check_layer_route(const msa_bank *b, bool need_qr, const void *QR, int32_t n_q, int32_t T, int32_t t_r,
+                      int32_t L_loc, int32_t h_q, int32_t k, const float *s_doc, const void *ws, size_t ws_bytes) {
+  int rc = check_bank(b);
+  if (rc) return rc;
+  if (need_qr) {
+    rc = check_route_args(QR, n_q, t_r);
+    if (rc) return rc;
+  } else if (n_q < 1 || t_r < 1) {
+    return fail(MSA_ERR_ARG, "n_q = %d, t_r = %d", n_q, t_r);
+  }
+  if (n_q > 65535) return fail(MSA_ERR_ARG, "n_q = %d > 65535", n_q);
+  if (s_doc && !aligned(s_doc, 4)) return fail(MSA_ERR_ARG, "s_doc is not 4-byte aligned");
+  if (T < 1 || L_loc < T || h_q < 1 || k < 1 || k > b->n_docs || k > 256 || h_q < b->h_kv || h_q % b->h_kv)
+    return fail(MSA_ERR_ARG, "T = %d, L_loc = %d, h_q = %d, k = %d", T, L_loc, h_q, k);
+  const LayerWs lw = layer_ws(b, n_q, T, t_r, L_loc, h_q, k);
+  if (!ws || ws_bytes < lw.total || !aligned(ws, 256))
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", lw.total, ws_bytes);
+  return 0;
+}
+
+int check_layer_tail(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, int32_t n_q, int32_t T,
+                     int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0, float scale, const msa_rope *rope,
+                     const void *O, const int32_t *idx, const float *val) {
+  const int rc = check_attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O);
+  if (rc) return rc;
+  CHECK_PTR(idx, 4, "idx");
+  CHECK_PTR(val, 4, "val");
+  return 0;
+}
+
+// One layer call's sizes, workspace and stream.  Workspace layout: document
+// scores (or order-preserving keys), the router scan's scratch (per-tile
+// records or inverse query norms), the top-k candidates, the attention's
+// split partials.
+struct LayerCtx {
+  const msa_bank *b;
+  int32_t n_q, T, t_r, L_loc, h_q, k;
+  char *w;
+  LayerWs lw;
+  hipStream_t s;
+  void *const *ev;
+  void *rt_ws() const { return w + lw.scores; }
+  void *tk_ws() const { return w + lw.scores + lw.route; }
+  void *at_ws() const { return w + lw.scores + lw.route + lw.topk; }
+  hipError_t rec(int i) const { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; }
+  // single-writer scan: the scores live in s_doc when given, else at the workspace's start
+  float *scores(float *s_doc) const { return s_doc ? s_doc : reinterpret_cast<float *>(w); }
+};
+
+// First half: the router scan.  Single-writer scans store the scores of the
+// documents inside one tile and per-tile edge records; otherwise the
+// document keys are zeroed and maxed atomically.
+hipError_t layer_route(const LayerCtx &c, const void *QR, float *s_doc) {
+  hipError_t e = hipSuccess;
+  if (msa::route_single_writer(c.t_r)) {
+    msa::RouteArgs ra = route_args(c.b, QR, c.n_q, c.t_r, static_cast<float *>(c.rt_ws()), c.scores(s_doc), nullptr,
+                                   nullptr);
+    e = c.rec(0);
+    if (e == hipSuccess) e = msa::launch_route_scan(ra, c.s);
+  } else {
+    uint32_t *keys = reinterpret_cast<uint32_t *>(c.w);
+    e = msa::launch_fill_u32(keys, (size_t)c.n_q * c.b->n_docs, 0u, c.s);
+    if (e == hipSuccess) e = c.rec(0);
+    msa::RouteArgs ra = route_args(c.b, QR, c.n_q, c.t_r, nullptr, nullptr, keys, nullptr);
+    ra.qinv = static_cast<float *>(c.rt_ws());
+    if (e == hipSuccess) e = msa::launch_route_scan(ra, c.s);
+  }
+  if (e == hipSuccess) e = c.rec(1);
+  return e;
+}
+
+// Second half: complete the document scores, select the top-k, attend.
+hipError_t layer_tail(const LayerCtx &c, const void *Q, const void *K_loc, const void *V_loc, int32_t pos0,
+                      float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc) {
+  const msa_bank *b = c.b;
+  hipError_t e = hipSuccess;
+  int n_fused = 0;  // > 0: the attention selects from this many candidates per query
+  if (msa::route_single_writer(c.t_r)) {
+    float *scores = c.scores(s_doc);
+    msa::RouteArgs ra = route_args(b, nullptr, c.n_q, c.t_r, static_cast<float *>(c.rt_ws()), scores, nullptr,
+                                   nullptr);
+    // documents on tile edges come from the scan's records: a single-pass
+    // top-k resolves them as it loads, the sliced one after a resolve kernel
+    // (coalesced over queries)
+    msa::TopkSrc src{};
+    src.scores = scores;
+    if (msa::topk_single_pass(b->n_docs)) {
+      src.mode = msa::TopkSrc::EDGES;
+      src.edges = ra.edges;
+      src.doc_chunk_off = b->doc_chunk_off;
+      src.n_tiles = (b->n_chunks + 15) / 16;
+      src.t_r = c.t_r;
+    } else {
+      src.mode = msa::TopkSrc::SCORES;
+      e = msa::launch_resolve_docs(ra, c.s);
+    }
+    // small k over a sliced bank: pass 1 here, the final selection of each
+    // query inside the attention workgroups (one kernel less)
+    n_fused = msa::topk_single_pass(b->n_docs) ? 0 : msa::topk_fused_candidates(b->n_docs, c.k);
+    if (n_fused > 0) {
+      if (e == hipSuccess) e = msa::launch_topk_pass1(src, c.n_q, b->n_docs, c.k, c.tk_ws(), c.s);
+    } else {
+      if (e == hipSuccess) e = msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
+    }
+    if (e == hipSuccess) e = c.rec(2);
+  } else {
+    uint32_t *keys = reinterpret_cast<uint32_t *>(c.w);
+    msa::TopkSrc src{};
+    src.mode = msa::TopkSrc::KEYS;
+    src.keys = keys;
+    e = msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
+    if (e == hipSuccess) e = c.rec(2);
+    const size_t nd = (size_t)c.n_q * b->n_docs;
+    if (e == hipSuccess && s_doc) {
+      e = hipMemcpyAsync(s_doc, keys, nd * sizeof(uint32_t), hipMemcpyDeviceToDevice, c.s);
+      if (e == hipSuccess) e = msa::launch_keys_to_scores(reinterpret_cast<uint32_t *>(s_doc), nd, c.s);
+    }
+  }
+  if (e == hipSuccess) {
+    msa::AttendArgs aa = attend_args(b, Q, K_loc, V_loc, c.n_q, c.T, c.L_loc, c.h_q, idx, c.k, pos0, scale, rope, O);
+    if (n_fused > 0) {
+      aa.cand = static_cast<const uint64_t *>(c.tk_ws());
+      aa.n_cand = n_fused;
+      aa.idx_out = idx;
+      aa.val_out = val;
+    }
+    e = msa::launch_attend(aa, c.at_ws(), c.s);
+  }
+  if (e == hipSuccess) e = c.rec(3);
+  return e;
+}
+
+}  // namespace
+
 extern "C" {
 
 int msa_abi_version(void) { return MSA_ABI_VERSION; }
@@ -444,94 +583,50 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
                       float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
                       size_t ws_bytes, void *const *stage_events, void *stream) {
   try {
-    int rc = check_bank(b);
+    int rc = check_layer_route(b, true, QR, n_q, T, t_r, L_loc, h_q, k, s_doc, ws, ws_bytes);
     if (rc) return rc;
-    rc = check_route_args(QR, n_q, t_r);
+    rc = check_layer_tail(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O, idx, val);
     if (rc) return rc;
-    rc = check_attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O);
-    if (rc) return rc;
-    if (n_q > 65535) return fail(MSA_ERR_ARG, "n_q = %d > 65535", n_q);
-    CHECK_PTR(idx, 4, "idx");
-    CHECK_PTR(val, 4, "val");
-    if (s_doc && !aligned(s_doc, 4)) return fail(MSA_ERR_ARG, "s_doc is not 4-byte aligned");
     if (stage_events)
       for (int i = 0; i < 4; ++i)
         if (!stage_events[i]) return fail(MSA_ERR_ARG, "stage_events[%d] is null", i);
-    const LayerWs lw = layer_ws(b, n_q, T, t_r, L_loc, h_q, k);
-    if (!ws || ws_bytes < lw.total || !aligned(ws, 256))
-      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu", lw.total, ws_bytes);
-    hipStream_t s = (hipStream_t)stream;
-    char *w = static_cast<char *>(ws);
-    void *rt_ws = w + lw.scores;
-    void *tk_ws = static_cast<char *>(rt_ws) + lw.route;
-    void *at_ws = static_cast<char *>(tk_ws) + lw.topk;
-    const size_t nd = (size_t)n_q * b->n_docs;
-    auto rec = [&](int i) -> hipError_t {
-      return stage_events ? hipEventRecord((hipEvent_t)stage_events[i], s) : hipSuccess;
-    };
-    hipError_t e = hipSuccess;
-    int n_fused = 0;  // > 0: the attention selects from this many candidates per query
-    if (msa::route_single_writer(t_r)) {
-      // scores written once per document: no zero fill, no keys
-      float *scores = s_doc ? s_doc : reinterpret_cast<float *>(w);
-      msa::RouteArgs ra = route_args(b, QR, n_q, t_r, static_cast<float *>(rt_ws), scores, nullptr, nullptr);
-      e = rec(0);
-      if (e == hipSuccess) e = msa::launch_route_scan(ra, s);
-      if (e == hipSuccess) e = rec(1);
-      // documents on tile edges come from the scan's records: a single-pass
-      // top-k resolves them as it loads, the sliced one after a resolve kernel
-      // (coalesced over queries)
-      msa::TopkSrc src{};
-      src.scores = scores;
-      if (msa::topk_single_pass(b->n_docs)) {
-        src.mode = msa::TopkSrc::EDGES;
-        src.edges = ra.edges;
-        src.doc_chunk_off = b->doc_chunk_off;
-        src.n_tiles = (b->n_chunks + 15) / 16;
-        src.t_r = t_r;
-      } else {
-        src.mode = msa::TopkSrc::SCORES;
-        if (e == hipSuccess) e = msa::launch_resolve_docs(ra, s);
-      }
-      // small k over a sliced bank: pass 1 here, the final selection of each
-      // query inside the attention workgroups (one kernel less)
-      n_fused = msa::topk_single_pass(b->n_docs) ? 0 : msa::topk_fused_candidates(b->n_docs, k);
-      if (n_fused > 0) {
-        if (e == hipSuccess) e = msa::launch_topk_pass1(src, n_q, b->n_docs, k, tk_ws, s);
-      } else {
-        if (e == hipSuccess) e = msa::launch_topk(src, n_q, b->n_docs, k, idx, val, tk_ws, s);
-      }
-      if (e == hipSuccess) e = rec(2);
-    } else {
-      uint32_t *keys = reinterpret_cast<uint32_t *>(w);
-      e = msa::launch_fill_u32(keys, nd, 0u, s);
-      if (e == hipSuccess) e = rec(0);
-      msa::RouteArgs ra = route_args(b, QR, n_q, t_r, nullptr, nullptr, keys, nullptr);
-      ra.qinv = static_cast<float *>(rt_ws);
-      if (e == hipSuccess) e = msa::launch_route_scan(ra, s);
-      if (e == hipSuccess) e = rec(1);
-      msa::TopkSrc src{};
-      src.mode = msa::TopkSrc::KEYS;
-      src.keys = keys;
-      if (e == hipSuccess) e = msa::launch_topk(src, n_q, b->n_docs, k, idx, val, tk_ws, s);
-      if (e == hipSuccess) e = rec(2);
-      if (e == hipSuccess && s_doc) {
-        e = hipMemcpyAsync(s_doc, keys, nd * sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
-        if (e == hipSuccess) e = msa::launch_keys_to_scores(reinterpret_cast<uint32_t *>(s_doc), nd, s);
-      }
-    }
-    if (e == hipSuccess) {
-      msa::AttendArgs aa = attend_args(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, idx, k, pos0, scale, rope, O);
-      if (n_fused > 0) {
-        aa.cand = static_cast<const uint64_t *>(tk_ws);
-        aa.n_cand = n_fused;
-        aa.idx_out = idx;
-        aa.val_out = val;
-      }
-      e = msa::launch_attend(aa, at_ws, s);
-    }
-    if (e == hipSuccess) e = rec(3);
+    const LayerCtx c{b, n_q, T, t_r, L_loc, h_q, k, static_cast<char *>(ws), layer_ws(b, n_q, T, t_r, L_loc, h_q, k),
+                     (hipStream_t)stream, stage_events};
+    hipError_t e = layer_route(c, QR, s_doc);
+    if (e == hipSuccess) e = layer_tail(c, Q, K_loc, V_loc, pos0, scale, rope, O, idx, val, s_doc);
     return e == hipSuccess ? ok() : dev_fail(e, "layer_forward");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+int msa_layer_route(const msa_bank *b, const void *QR, int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc,
+                    int32_t h_q, int32_t k, float *s_doc, void *ws, size_t ws_bytes, void *stream) {
+  try {
+    const int rc = check_layer_route(b, true, QR, n_q, T, t_r, L_loc, h_q, k, s_doc, ws, ws_bytes);
+    if (rc) return rc;
+    const LayerCtx c{b, n_q, T, t_r, L_loc, h_q, k, static_cast<char *>(ws), layer_ws(b, n_q, T, t_r, L_loc, h_q, k),
+                     (hipStream_t)stream, nullptr};
+    const hipError_t e = layer_route(c, QR, s_doc);
+    return e == hipSuccess ? ok() : dev_fail(e, "layer_route");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+int msa_layer_select_attend(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, int32_t n_q,
+                            int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0, float scale,
+                            const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
+                            size_t ws_bytes, void *stream) {
+  try {
+    int rc = check_layer_route(b, false, nullptr, n_q, T, t_r, L_loc, h_q, k, s_doc, ws, ws_bytes);
+    if (rc) return rc;
+    rc = check_layer_tail(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O, idx, val);
+    if (rc) return rc;
+    const LayerCtx c{b, n_q, T, t_r, L_loc, h_q, k, static_cast<char *>(ws), layer_ws(b, n_q, T, t_r, L_loc, h_q, k),
+                     (hipStream_t)stream, nullptr};
+    const hipError_t e = layer_tail(c, Q, K_loc, V_loc, pos0, scale, rope, O, idx, val, s_doc);
+    return e == hipSuccess ? ok() : dev_fail(e, "layer_select_attend");
   } catch (...) {
     return fail(MSA_ERR_DEVICE, "internal error");
   }

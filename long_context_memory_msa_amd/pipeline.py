@@ -17,6 +17,12 @@ asynchronous prefetch; wiselychen blog, mechanism 3); with a tiered bank
 different resource from the scan's HBM stream, and the same two streams
 overlap it.
 
+(msa_layer_route / msa_layer_select_attend would split the layer the same
+way; measured here they make the pipelined step 25-30 us slower: the
+resolve kernel then runs in the tail, starved by the scan, and the
+attention's in-kernel selection lengthens the part that cannot share the
+compute units with the scan.)
+
 Outputs rotate over `slots` buffers: step s writes slot s % slots, which
 stays valid until step s + slots is issued.  The route stream never waits on
 the GPU: before reusing a slot the host waits for the tail that last read it

@@ -207,3 +207,24 @@ def test_layer_validation():
     assert _code(msa.msa_layer_forward, *bad, stream=0) == L.MSA_ERR_ARG
     assert _code(msa.msa_layer_forward, *args, stage_events=[A.addr, 0, A.addr, A.addr], stream=0) == L.MSA_ERR_ARG
     assert msa.msa_layer_workspace_bytes(b, 1, 4, 4, 8, 32, 2) > 0
+
+
+def test_layer_halves_validation():
+    # the two halves check the same sizes and the same workspace as the whole layer
+    b = _bank()
+    r = _rope()
+    big = 1 << 30
+    route = [b, A, 1, 4, 4, 8, 32, 2, None, A]
+    assert _code(msa.msa_layer_route, *route, 16, stream=0) == L.MSA_ERR_WORKSPACE
+    assert _code(msa.msa_layer_route, b, None, *route[2:], big, stream=0) == L.MSA_ERR_ARG     # QR
+    assert _code(msa.msa_layer_route, b, A, 1, 4, 0, 8, 32, 2, None, A, big, stream=0) == L.MSA_ERR_ARG  # t_r
+    assert _code(msa.msa_layer_route, b, A, 1, 9, 4, 8, 32, 2, None, A, big, stream=0) == L.MSA_ERR_ARG  # T > L_loc
+    assert _code(msa.msa_layer_route, b, A, 1, 4, 4, 8, 32, 5, None, A, big, stream=0) == L.MSA_ERR_ARG  # k > n_docs
+    tail = [b, A, A, A, 1, 4, 4, 8, 32, 2, 2, 0.1, r, A, A, A, None, A]
+    assert _code(msa.msa_layer_select_attend, *tail, 16, stream=0) == L.MSA_ERR_WORKSPACE
+    bad = list(tail)
+    bad[14] = None                                          # idx
+    assert _code(msa.msa_layer_select_attend, *bad, big, stream=0) == L.MSA_ERR_ARG
+    bad = list(tail)
+    bad[12] = _rope(max_pos=4)                              # rope shorter than pos0 + L_loc
+    assert _code(msa.msa_layer_select_attend, *bad, big, stream=0) == L.MSA_ERR_ARG

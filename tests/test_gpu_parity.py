@@ -348,6 +348,44 @@ def test_layer_equals_composition_and_is_deterministic(device):
     assert torch.equal(s_doc, s1) and torch.equal(idx, i1) and torch.equal(val, v1) and torch.equal(out, o1)
 
 
+def _layer_halves(bank, rope, w, QR, Q, Kl, Vl, device):
+    """msa_layer_route on one stream, msa_layer_select_attend on another after an event."""
+    n_q = w.n_q
+    O_ = torch.empty((n_q, w.T, w.h_q, w.d), dtype=M.TORCH_DTYPE[w.dtype], device=device)
+    idx = torch.empty((n_q, w.k), dtype=torch.int32, device=device)
+    val = torch.empty((n_q, w.k), dtype=torch.float32, device=device)
+    s_doc = torch.empty((n_q, w.n_docs), dtype=torch.float32, device=device)
+    nb = L.msa_layer_workspace_bytes(bank.c, n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k)
+    ws = M.workspace(nb, device)
+    rs, ts = torch.cuda.Stream(device=device), torch.cuda.Stream(device=device)
+    rs.wait_stream(torch.cuda.current_stream())
+    L.msa_layer_route(bank.c, QR, n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, s_doc, ws, nb, rs)
+    ev = torch.cuda.Event()
+    ev.record(rs)
+    ts.wait_event(ev)
+    L.msa_layer_select_attend(bank.c, Q, Kl, Vl, n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0,
+                              L.default_scale(w.d), rope.c, O_, idx, val, s_doc, ws, nb, ts)
+    torch.cuda.synchronize()
+    return O_, idx, val, s_doc
+
+
+# the halves against the whole layer: single-writer scan with single-pass top-k
+# (cfg3 small), many-row tiled scan (cfg1, 128 router rows), atomic keys
+# (cfg1, 5 router rows), and the fp32 decode scan (cfg0)
+@pytest.mark.parametrize("name,t_r", [("cfg3", 1), ("cfg1", 128), ("cfg1", 5), ("cfg0", 16)])
+def test_layer_halves_equal_layer_forward(device, name, t_r):
+    cfg, bt = SMALL[name]
+    w = _wl(cfg, bt, T_route=t_r)
+    log(f"layer halves {name} t_r={t_r} docs={w.n_docs}")
+    qi, K, V, KR = host_inputs(w)
+    bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
+    QR, Q, Kl, Vl = query_views(w, qi, device)
+    want = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+    got = _layer_halves(bank, rope, w, QR, Q, Kl, Vl, device)
+    for x, y in zip(got, want):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("k", [16, 32])
 def test_layer_sliced_topk_selected_in_attention(device, k):
     # more documents than one top-k workgroup holds (8,192), small k: the layer
@@ -377,6 +415,8 @@ def test_layer_sliced_topk_selected_in_attention(device, k):
                         rope.c, out, M.workspace(nb2, device), nb2)
     torch.cuda.synchronize()
     assert torch.equal(s_doc, s1) and torch.equal(idx, i1) and torch.equal(val, v1) and torch.equal(out, o1)
+    for x, y in zip(_layer_halves(bank, rope, w, QR, Q, Kl, Vl, device), (o1, i1, v1, s1)):
+        assert torch.equal(x, y)
     want = O.layer_forward(qi["QR"][:, w.L_loc - w.T_route:w.L_loc], qi["Q"][:, w.L_loc - w.T:w.L_loc],
                            qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], ob, w.k, w.pos0, base=w.rope_base)
     assert np.abs(host(s1) - want["s_doc"]).max() <= 2e-3
