@@ -579,6 +579,21 @@ def main() -> int:
     layer = [ev.ms(ev.h[4 * i], ev.h[4 * i + 3]) for i in range(args.steps)]
     ev.close()
 
+    # the scan's access pattern without its arithmetic (read-only probe), same launches
+    n_probe = max(10, args.steps // 2)
+    pws_n = (w.n_chunks + 15) // 16 * 128
+    pws = M.workspace(pws_n, dev)
+    for _ in range(3):
+        L.msa_scan_read_probe(bank.c, pws, pws_n)
+    pev = Events(2 * n_probe)
+    for i in range(n_probe):
+        torch.cuda.current_stream().record_event(pev.ev[2 * i])
+        L.msa_scan_read_probe(bank.c, pws, pws_n)
+        torch.cuda.current_stream().record_event(pev.ev[2 * i + 1])
+    torch.cuda.synchronize()
+    probe_ms = statistics.median(pev.ms(pev.h[2 * i], pev.h[2 * i + 1]) for i in range(n_probe))
+    pev.close()
+
     # planted gold documents must be among each query's selection
     gi = idx.cpu().numpy()
     gold_ok = float(np.mean([set(w.gold[q].tolist()) <= set(gi[q].tolist()) for q in range(w.n_q)]))
@@ -623,7 +638,11 @@ def main() -> int:
         "route_tokens_per_s": w.n_tok / (route_ms * 1e-3),
         "roofline": {"bound": "hbm", "kernel": "route_scan", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": route_traffic(scan_bytes),
-                     "bytes_per_launch": scan_bytes},
+                     "bytes_per_launch": scan_bytes,
+                     "pattern_floor": {"kernel": "scan_read_probe", "ms": probe_ms,
+                                       "GB/s": scan_bytes / (probe_ms * 1e-3) / 1e9,
+                                       "frac_of_peak": scan_bytes / (probe_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "scan_frac_of_floor": probe_ms / route_ms}},
         "pool": {"slabs": enc["slabs"], "GB/s": pool_gbs, "frac": pool_gbs / HBM_PEAK_GBS},
         "gold_recovered": gold_ok,
     }

@@ -248,6 +248,19 @@ int msa_sparse_attend(const msa_bank *b, const void *Q, const void *K_loc, const
                       int32_t L_loc, int32_t h_q, const int32_t *idx, int32_t k, int32_t pos0, float scale,
                       const msa_rope *rope, void *O, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Measurement aid (no part of the method): reads the bank's router keys,
+ * inverse norms and chunk->document ids with exactly the access pattern,
+ * grid and tile order of the decode router scan (t_r = 1), without its
+ * arithmetic, and writes one 128-byte record per 16-chunk tile into ws.  Its
+ * duration is the practical floor of msa_route_score's scan on this device
+ * (the nominal HBM peak is not reachable by any access pattern); bench.py
+ * reports the scan against both.  bf16 banks with h_r = 8, d_r = 128 only
+ * (else MSA_ERR_UNSUPPORTED).  ws: at least ceil(n_chunks / 16) * 128 bytes,
+ * 16-byte aligned, contents overwritten (MSA_ERR_WORKSPACE otherwise).
+ */
+int msa_scan_read_probe(const msa_bank *b, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes msa_layer_forward needs for these sizes (0 on invalid sizes). */
 size_t msa_layer_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q,
                                  int32_t k);

@@ -77,6 +77,7 @@ def _load():
         "msa_layer_workspace_bytes": ([bank_p, I32, I32, I32, I32, I32, I32], SZ),
         "msa_layer_forward": ([bank_p, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, rope_p, P, P, P, P, P, SZ,
                                P, P], ctypes.c_int),
+        "msa_scan_read_probe": ([bank_p, P, SZ, P], ctypes.c_int),
         "msa_layer_route": ([bank_p, P, I32, I32, I32, I32, I32, I32, P, P, SZ, P], ctypes.c_int),
         "msa_layer_select_attend": ([bank_p, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, rope_p, P, P, P, P, P, SZ,
                                      P], ctypes.c_int),
@@ -200,6 +201,10 @@ def msa_layer_forward(bank: MsaBank, Q, K_loc, V_loc, QR, n_q: int, T: int, t_r:
     _check(_lib.msa_layer_forward(ctypes.byref(bank), _ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(QR), n_q, T, t_r,
                                   L_loc, h_q, k, pos0, scale, ctypes.byref(rope), _ptr(O), _ptr(idx), _ptr(val),
                                   _ptr(s_doc), _ptr(ws), ws_bytes, ev, _stream(stream)))
+
+
+def msa_scan_read_probe(bank: MsaBank, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.msa_scan_read_probe(ctypes.byref(bank), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def msa_layer_route(bank: MsaBank, QR, n_q: int, T: int, t_r: int, L_loc: int, h_q: int, k: int, s_doc, ws,

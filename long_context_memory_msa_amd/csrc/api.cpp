@@ -515,6 +515,23 @@ int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r,
   }
 }
 
+int msa_scan_read_probe(const msa_bank *b, void *ws, size_t ws_bytes, void *stream) {
+  try {
+    const int rc = check_bank(b);
+    if (rc) return rc;
+    if (b->dtype != MSA_BF16 || b->h_r != 8 || b->d_r != 128)
+      return fail(MSA_ERR_UNSUPPORTED, "the probe mirrors the bf16 scan with 8 router heads of 128");
+    const size_t need = (size_t)((b->n_chunks + 15) / 16) * 32 * sizeof(float);
+    if (!ws || ws_bytes < need || !aligned(ws, 16))
+      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
+    const msa::RouteArgs a = route_args(b, nullptr, 1, 1, static_cast<float *>(ws), nullptr, nullptr, nullptr);
+    const hipError_t e = msa::launch_scan_read_probe(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : dev_fail(e, "scan_read_probe");
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
 size_t msa_topk_workspace_bytes(int32_t n_q, int32_t n_docs, int32_t k) {
   if (n_q < 1 || n_docs < 1 || k < 1 || k > 256 || k > n_docs) return 0;
   return msa::topk_ws_bytes(n_q, n_docs, k);

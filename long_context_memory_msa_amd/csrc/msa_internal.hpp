@@ -58,6 +58,9 @@ size_t route_wide_ws_bytes(int n_q, int t_r, int h_r);
 size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_q, int t_r);
 hipError_t launch_route_wide(const RouteArgs &a, hipStream_t s);
 hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s);
+// read-only probe of the decode scan's traffic (bf16, 8 x 128 router heads);
+// writes one record per 16-chunk tile to a.edges
+hipError_t launch_scan_read_probe(const RouteArgs &a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);
 hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s);  // in place

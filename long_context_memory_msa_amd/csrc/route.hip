@@ -342,6 +342,38 @@ __global__ void resolve_docs_kernel(const float *edges, const int64_t *doc_chunk
   if (edge_doc_score(edges, doc_chunk_off, n_tiles, t_r, q, doc, &v)) *out = v;
 }
 
+// Bandwidth probe: the decode scan's memory traffic without its arithmetic.
+// Same persistent grid and tile order, the same 16-byte loads of each tile's
+// key rows (8 in flight per wave), the same inverse-norm and document-id
+// loads and one 128-byte record written per tile; the loaded words are only
+// XOR-folded.  Its time is the practical floor of the scan on this device.
+template <int HR, int DR>
+__global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void scan_read_probe_kernel(RouteArgs a, int64_t n_tiles,
+                                                                                 int64_t n_waves) {
+  constexpr int SEG = DR * 2 / 64;  // 64-byte segments per head row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, G = lane >> 4;
+  const bf16_t *krbar = static_cast<const bf16_t *>(a.krbar);
+  uint32_t acc = 0;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < n_tiles; tile += n_waves) {
+    int64_t cp = tile * 16 + col;
+    cp = cp < a.n_chunks ? cp : a.n_chunks - 1;
+    const uint4 *row = reinterpret_cast<const uint4 *>(krbar + cp * (HR * DR)) + G;
+    const float *ip = a.kr_inv_norm + cp * HR;
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < HR; ++j) m += ip[j];
+    const int d = a.chunk_doc[cp];
+#pragma unroll 8
+    for (int i = 0; i < HR * SEG; ++i) {
+      const uint4 v = row[4 * i];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    acc ^= __float_as_uint(m) ^ (uint32_t)d;
+    if (lane < 32) a.edges[tile * 32 + lane] = __uint_as_float(acc & 0x3FFFFFFFu);
+  }
+}
+
 template <typename T, int HR, int DR, bool EDGE>
 hipError_t route_launch(const RouteArgs &a, hipStream_t s) {
   // Persistent grid: exactly as many workgroups as stay resident together
@@ -411,6 +443,22 @@ hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s) {
 }
 
 bool route_single_writer(int t_r) { return t_r == 1 || t_r == 16; }
+
+hipError_t launch_scan_read_probe(const RouteArgs &a, hipStream_t s) {
+  if (a.n_chunks == 0) return hipSuccess;
+  if (a.dtype != 1 || a.h_r != 8 || a.d_r != 128) return hipErrorInvalidValue;
+  // the decode scan's grid (one row block): resident workgroups, balanced
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, route_scan_kernel<bf16_t, 8, 128, true>, 256, 0) != hipSuccess ||
+      n < 1)
+    n = 1;
+  const int64_t n_tiles = (a.n_chunks + 15) / 16;
+  int64_t wgs = std::min<int64_t>((int64_t)device_cu_count() * n, (n_tiles + 3) / 4);
+  const int64_t rounds = (n_tiles + 4 * wgs - 1) / (4 * wgs);
+  wgs = (n_tiles + 4 * rounds - 1) / (4 * rounds);
+  hipLaunchKernelGGL((scan_read_probe_kernel<8, 128>), dim3((unsigned)wgs), dim3(256), 0, s, a, n_tiles, wgs * 4);
+  return hipGetLastError();
+}
 
 size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_q, int t_r) {
   if (route_single_writer(t_r)) {

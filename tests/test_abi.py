@@ -228,3 +228,12 @@ def test_layer_halves_validation():
     bad = list(tail)
     bad[12] = _rope(max_pos=4)                              # rope shorter than pos0 + L_loc
     assert _code(msa.msa_layer_select_attend, *bad, big, stream=0) == L.MSA_ERR_ARG
+
+
+def test_scan_read_probe_validation():
+    b = _bank()
+    need = (b.n_chunks + 15) // 16 * 128
+    assert _code(msa.msa_scan_read_probe, b, A, need - 1, stream=0) == L.MSA_ERR_WORKSPACE
+    assert _code(msa.msa_scan_read_probe, b, None, need, stream=0) == L.MSA_ERR_WORKSPACE
+    assert _code(msa.msa_scan_read_probe, _bank(dtype=L.MSA_F32), A, need, stream=0) == L.MSA_ERR_UNSUPPORTED
+    assert _code(msa.msa_scan_read_probe, _bank(h_r=4), A, need, stream=0) == L.MSA_ERR_UNSUPPORTED

@@ -432,6 +432,19 @@ def test_layer_sliced_topk_selected_in_attention(device, k):
     assert_attention_close(host(o1), o_ref)
 
 
+def test_scan_read_probe_runs(device):
+    # the bandwidth probe reads the bank in the scan's pattern and writes one
+    # finite record per 16-chunk tile (its values carry no meaning)
+    w = _wl(3, 700_000)
+    qi, K, V, KR = host_inputs(w)
+    bank, _ = gpu_bank_pooled(w, K, V, KR, device, 1)
+    n_tiles = (w.n_chunks + 15) // 16
+    ws = torch.full((n_tiles * 32,), float("nan"), dtype=torch.float32, device=device)
+    L.msa_scan_read_probe(bank.c, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ws).all()
+
+
 def test_interleave_small(device):
     # the interleave driver on 2 layers of a small bank against the oracle's loop
     from long_context_memory_msa_amd.interleave import interleave
