@@ -495,9 +495,9 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); the bank would shard by whole documents across GPUs, see DESIGN.md.",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); a bank would shard by whole documents, one shard per GPU, with a "
+              f"global top-k merge of the per-GPU candidates.", file=sys.stderr)
         return 2
 
     import numpy as np

@@ -14,7 +14,7 @@ give it.  Sources (cited by page title and section, never by line):
 * [CS] gitcode/CSDN article on MSA ("four technical breakthroughs").
 * [WC] wiselychen blog, "MSA: 4B model beats a 235B RAG system".
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   R1 document score = max over the document's chunk scores;
   R2 RoPE is applied to K and Q only (not V, not the router vectors K^R/Q^R);
   R3 RoPE is applied per token at its in-document position, before pooling;
