@@ -432,6 +432,37 @@ def test_layer_sliced_topk_selected_in_attention(device, k):
     assert_attention_close(host(o1), o_ref)
 
 
+# degenerate banks through the whole layer against the oracle: a single
+# one-token document, a bank smaller than one 16-chunk tile with every
+# document selected, documents ending exactly on tile edges, and one long
+# document spanning many tiles among short ones; decode (one router token)
+# and many-row (32 router tokens) scans
+@pytest.mark.parametrize("lens,k,t_r", [
+    ([1], 1, 1), ([1], 1, 32),
+    ([3, 200, 129, 1, 64], 5, 1), ([3, 200, 129, 1, 64], 5, 32),
+    ([16 * 128] * 3 + [128] * 5, 4, 1),
+    ([40, 100 * 128 + 7, 300, 2, 4000], 3, 1), ([40, 100 * 128 + 7, 300, 2, 4000], 3, 32)])
+def test_layer_degenerate_banks(device, lens, k, t_r):
+    lens = np.asarray(lens, dtype=np.int64)
+    n_q = 2
+    w = _wl(1, None, doc_lens=lens, k=k, pos0=k, n_q=n_q, T=8, L_loc=max(32, t_r), T_route=t_r,
+            gold=np.zeros((n_q, 0), np.int64))
+    log(f"degenerate bank lens={lens.tolist()} k={k} t_r={t_r} chunks={w.n_chunks}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    want = O.layer_forward(qi["QR"][:, w.L_loc - w.T_route:w.L_loc], qi["Q"][:, w.L_loc - w.T:w.L_loc],
+                           qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], ob, w.k, w.pos0, base=w.rope_base)
+    bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
+    QR, Q, Kl, Vl = query_views(w, qi, device)
+    out, idx, val, s_doc = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+    assert np.abs(host(s_doc) - want["s_doc"]).max() <= 2e-3
+    gi = idx.cpu().numpy()
+    topk_set_valid(gi, want["s_doc"], w.k)
+    o_ref = O.attend(qi["Q"][:, w.L_loc - w.T:w.L_loc], qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc],
+                     ob["kbar"], ob["vbar"], ob["doc_chunk_off"], gi, w.pos0, base=w.rope_base)
+    assert_attention_close(host(out), o_ref)
+
+
 def test_scan_read_probe_runs(device):
     # the bandwidth probe reads the bank in the scan's pattern and writes one
     # finite record per 16-chunk tile (its values carry no meaning)
