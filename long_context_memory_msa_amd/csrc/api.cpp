@@ -267,10 +267,18 @@ hipError_t layer_route(const LayerCtx &c, const void *QR, float *s_doc) {
     if (e == hipSuccess) e = msa::launch_route_scan(ra, c.s);
   } else {
     uint32_t *keys = reinterpret_cast<uint32_t *>(c.w);
-    e = msa::launch_fill_u32(keys, (size_t)c.n_q * c.b->n_docs, 0u, c.s);
-    if (e == hipSuccess) e = c.rec(0);
+    const size_t nd = (size_t)c.n_q * c.b->n_docs;
     msa::RouteArgs ra = route_args(c.b, QR, c.n_q, c.t_r, nullptr, nullptr, keys, nullptr);
     ra.qinv = static_cast<float *>(c.rt_ws());
+    if (msa::route_use_wide(c.b->dtype, c.b->h_r, c.b->d_r, c.t_r)) {
+      // the many-row scan's pre-kernel zeroes the keys
+      ra.zero = keys;
+      ra.n_zero = (int64_t)nd;
+      e = c.rec(0);
+    } else {
+      e = msa::launch_fill_u32(keys, nd, 0u, c.s);
+      if (e == hipSuccess) e = c.rec(0);
+    }
     if (e == hipSuccess) e = msa::launch_route_scan(ra, c.s);
   }
   if (e == hipSuccess) e = c.rec(1);

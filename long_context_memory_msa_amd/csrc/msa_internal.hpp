@@ -51,6 +51,10 @@ struct RouteArgs {
   uint32_t *chunk_out;
   // many-row (wide) scan: (1/h_r)/||Q^R|| per head and query row, [h_r][n_q * t_r] (workspace)
   float *qinv;
+  // many-row scan: words its pre-kernel sets to zero before the scan (the
+  // document keys, in place of a separate fill launch); null = none
+  uint32_t *zero = nullptr;
+  int64_t n_zero = 0;
 };
 bool route_single_writer(int t_r);                    // (query, document) scores have one writer
 bool route_use_wide(int dtype, int h_r, int d_r, int t_r);     // GEMM-tiled scan for many rows per query

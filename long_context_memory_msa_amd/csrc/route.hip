@@ -477,7 +477,7 @@ hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s) {
-  if (a.n_chunks == 0) return hipSuccess;
+  if (a.n_chunks == 0) return a.zero ? launch_fill_u32(a.zero, (size_t)a.n_zero, 0u, s) : hipSuccess;
   if (!a.edges && a.qinv && route_use_wide(a.dtype, a.h_r, a.d_r, a.t_r)) return launch_route_wide(a, s);
   if (a.dtype == 0) return a.d_r == 64 ? route_by_hr<float, 64>(a, s) : route_by_hr<float, 128>(a, s);
   if (a.d_r == 256) return route_by_hr<bf16_t, 256>(a, s);  // a router twice the head width

@@ -45,9 +45,13 @@ constexpr int MW = 128;  // rows per workgroup
 #endif
 constexpr int WIDE_NW = MSA_WIDE_NW;
 
-// qinv[h][row] = (1/H_r) / ||Q^R[row][h]|| (0 for a zero row); 16 lanes per (row, head)
+// qinv[h][row] = (1/H_r) / ||Q^R[row][h]|| (0 for a zero row); 16 lanes per
+// (row, head).  Also zeroes zero[0, n_zero) (the document keys the scan maxes
+// into), so the scan needs no separate fill launch.
 template <int DR>
-__global__ void q_inv_norm_kernel(const bf16_t *qr, int n_rows, int h_r, float *qinv) {
+__global__ void q_inv_norm_kernel(const bf16_t *qr, int n_rows, int h_r, float *qinv, uint32_t *zero, int64_t n_zero) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_zero; i += (int64_t)gridDim.x * blockDim.x)
+    zero[i] = 0u;
   const int n_pairs = n_rows * h_r;
   constexpr int SEGS = DR / 8;  // 16-byte segments per row slice
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -285,7 +289,7 @@ hipError_t launch_route_wide(const RouteArgs &a, hipStream_t s) {
   const int n_pairs = n_rows * a.h_r;
   const int64_t threads = (int64_t)n_pairs * (128 / 8);
   hipLaunchKernelGGL(q_inv_norm_kernel<128>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(a.qr), n_rows, a.h_r, a.qinv);
+                     static_cast<const bf16_t *>(a.qr), n_rows, a.h_r, a.qinv, a.zero, a.zero ? a.n_zero : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_mtiles = (n_rows + MW - 1) / MW;
