@@ -176,6 +176,7 @@ def test_route_head_shapes(device, dtype, h_r, d_r, t_r, n_q):
 
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n_q,n_docs,k", [(1, 7, 1), (1, 7, 7), (3, 2048, 16), (2, 5000, 256), (16, 23048, 16),
+                                          (2, 8192, 32), (1, 6000, 8), (3, 2049, 32), (2, 40, 32),
                                           (4, 4099, 64), (1, 300, 256), (1, 24576, 256),
                                           # above 24K documents per query: the two-pass path
                                           (2, 24577, 16), (3, 60000, 64), (1, 100000, 256)])
