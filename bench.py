@@ -13,9 +13,9 @@ A step is one pass of the routed layer over one batch of 16 queries: router
 scan with the fused document max, top-k, sparse attention (plus split merge).
 Two timed regions of --steps steps each: sequential msa_layer_forward calls
 on one stream (per-stage events: layer latency, the scan's HBM roofline), then
-independent batches through the two-stream decode pipeline, the top-k and
-attention of one batch running during the scan of the next; the pipelined
-rate is the throughput `value`.  Prints one JSON line.
+independent batches through the decode pipeline (two route streams whose
+scans overlap, the top-k and attention of earlier batches on a third); the
+pipelined rate is the throughput `value`.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -104,7 +104,7 @@ def attend_roofline(w, bank, gi, attend_ms: float) -> dict:
 
 
 def run_pipelined(bank, rope, w, scale, dev, QR, Q, Kl, Vl, idx, O_, args) -> float:
-    """Wall time of --steps independent decode steps through the two-stream
+    """Wall time of --steps independent decode steps through the decode
     pipeline; the last step's output must equal msa_layer_forward's."""
     import torch
 
@@ -384,8 +384,8 @@ def bench_append(args) -> int:
 def bench_tiered(args) -> int:
     """The 100M-token decode layer with a tiered bank: pooled keys/values in
     pinned host memory (read by the attention over the host link), router keys
-    in HBM.  Steps of the same query batch run through the two-stream pipeline
-    (attention of step s during the routing of step s+1); one sequential step
+    in HBM.  Steps of the same query batch run through the decode pipeline
+    (attention of step s during the routing of later steps); one sequential step
     with stage events gives the breakdown."""
     import numpy as np
     import torch
@@ -488,7 +488,7 @@ def main() -> int:
                     default="decode100m",
                     help="decode100m: the headline layer (default); interleave: 18 routed layers x 10M tokens, "
                          "3 Memory Interleave rounds (MFMA-bound prefill report); tiered: the decode layer with "
-                         "Kbar/Vbar in host memory, two-stream pipeline; append: the last 10%% of the documents "
+                         "Kbar/Vbar in host memory, decode pipeline; append: the last 10%% of the documents "
                          "appended to an encoded bank; project: the router projection GEMM")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
@@ -627,7 +627,9 @@ def main() -> int:
                    "bank_tokens": w.n_tok, "n_docs": w.n_docs, "n_chunks": w.n_chunks, "queries": w.n_q,
                    "query_tokens": w.T, "k": w.k, "chunk": w.chunk},
         "pipelined": (None if args.sequential_only else
-                      {"streams": 2, "overlap": "top-k + attention of step s during the router scan of step s+1"}),
+                      {"streams": 3, "overlap": "router scans of steps s and s+1 on two streams (grids capped at "
+                                                "one workgroup per CU), top-k + attention of earlier steps on a "
+                                                "third"}),
         "sequential": {"ms_per_step": ms_seq, "value": w.n_tok / (ms_seq * 1e-3)},
         "layer_latency_ms": statistics.median(layer),
         "stage_ms": {"route": statistics.median(route), "topk": statistics.median(topk),

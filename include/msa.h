@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 enum {
   MSA_OK = 0,
@@ -205,11 +205,16 @@ size_t msa_route_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t t_r);
  * (the document score is the max over its chunks; cosine 0 for a zero norm).
  * qr: [n_q][t_r][h_r][d_r] bank dtype; s_doc: [n_q][n_docs] fp32;
  * s_chunk: [n_q][n_chunks] fp32 or NULL; ws: msa_route_workspace_bytes bytes
- * (16-byte aligned; may be NULL when that is 0).  Errors: MSA_ERR_ARG,
- * MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE.
+ * (16-byte aligned; may be NULL when that is 0).  max_wg_per_cu: 0 sizes the
+ * streaming scan's persistent grid to every workgroup that stays resident
+ * (fastest when the scan runs alone); n >= 1 caps it at n workgroups per
+ * compute unit, which leaves room for kernels on other streams (a decode
+ * pipeline overlapping scans and the top-k/attention of earlier steps uses
+ * 1).  The results do not depend on it.  Errors: MSA_ERR_ARG (also
+ * max_wg_per_cu < 0), MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE.
  */
 int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *s_doc, float *s_chunk,
-                    void *ws, size_t ws_bytes, void *stream);
+                    void *ws, size_t ws_bytes, int32_t max_wg_per_cu, void *stream);
 
 /* Workspace bytes msa_topk needs for these sizes (0 on invalid sizes). */
 size_t msa_topk_workspace_bytes(int32_t n_q, int32_t n_docs, int32_t k);

@@ -45,7 +45,7 @@ class MsaBank(ctypes.Structure):
                 ("krbar", ctypes.c_void_p), ("kr_inv_norm", ctypes.c_void_p)]
 
 
-ABI_VERSION = 2  # include/msa.h MSA_ABI_VERSION
+ABI_VERSION = 3  # include/msa.h MSA_ABI_VERSION
 
 
 def _load():
@@ -68,7 +68,7 @@ def _load():
         "msa_rope_table": ([P, P, I32, I32, D, P], ctypes.c_int),
         "msa_pool_memory": ([bank_p, P, P, P, I32, I32, rope_p, P], ctypes.c_int),
         "msa_route_workspace_bytes": ([bank_p, I32, I32], SZ),
-        "msa_route_score": ([bank_p, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
+        "msa_route_score": ([bank_p, P, I32, I32, P, P, P, SZ, I32, P], ctypes.c_int),
         "msa_topk_workspace_bytes": ([I32, I32, I32], SZ),
         "msa_topk": ([P, I32, I32, I32, P, P, P, SZ, P], ctypes.c_int),
         "msa_attend_workspace_bytes": ([bank_p, I32, I32, I32, I32, I32], SZ),
@@ -164,9 +164,9 @@ def msa_route_workspace_bytes(bank: MsaBank, n_q: int, t_r: int) -> int:
 
 
 def msa_route_score(bank: MsaBank, QR, n_q: int, t_r: int, s_doc, s_chunk=None, ws=None, ws_bytes: int = 0,
-                    stream=None) -> None:
+                    stream=None, max_wg_per_cu: int = 0) -> None:
     _check(_lib.msa_route_score(ctypes.byref(bank), _ptr(QR), n_q, t_r, _ptr(s_doc), _ptr(s_chunk), _ptr(ws),
-                                ws_bytes, _stream(stream)))
+                                ws_bytes, max_wg_per_cu, _stream(stream)))
 
 
 def msa_topk_workspace_bytes(n_q: int, n_docs: int, k: int) -> int:

@@ -488,12 +488,13 @@ size_t msa_route_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t t_r) {
 }
 
 int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *s_doc, float *s_chunk,
-                    void *ws, size_t ws_bytes, void *stream) {
+                    void *ws, size_t ws_bytes, int32_t max_wg_per_cu, void *stream) {
   try {
     int rc = check_bank(b);
     if (rc) return rc;
     rc = check_route_args(qr, n_q, t_r);
     if (rc) return rc;
+    if (max_wg_per_cu < 0) return fail(MSA_ERR_ARG, "max_wg_per_cu must be >= 0");
     CHECK_PTR(s_doc, 4, "s_doc");
     if (s_chunk && !aligned(s_chunk, 4)) return fail(MSA_ERR_ARG, "s_chunk is not 4-byte aligned");
     const size_t need = msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, n_q, t_r);
@@ -505,6 +506,7 @@ int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r,
     hipError_t e;
     if (msa::route_single_writer(t_r)) {
       msa::RouteArgs a = route_args(b, qr, n_q, t_r, static_cast<float *>(ws), s_doc, nullptr, ck);
+      a.max_wg_per_cu = max_wg_per_cu;
       e = msa::launch_route_scan(a, s);
       if (e == hipSuccess) e = msa::launch_resolve_docs(a, s);
     } else {
@@ -513,6 +515,7 @@ int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r,
       if (e == hipSuccess && ck) e = msa::launch_fill_u32(ck, nc, 0u, s);
       msa::RouteArgs a = route_args(b, qr, n_q, t_r, nullptr, nullptr, dk, ck);
       a.qinv = static_cast<float *>(ws);
+      a.max_wg_per_cu = max_wg_per_cu;
       if (e == hipSuccess) e = msa::launch_route_scan(a, s);
       if (e == hipSuccess) e = msa::launch_keys_to_scores(dk, nd, s);
       if (e == hipSuccess && ck) e = msa::launch_keys_to_scores(ck, nc, s);

@@ -55,6 +55,9 @@ struct RouteArgs {
   // document keys, in place of a separate fill launch); null = none
   uint32_t *zero = nullptr;
   int64_t n_zero = 0;
+  // streaming scan: at most this many workgroups per compute unit in the
+  // persistent grid (0 = as many as stay resident)
+  int max_wg_per_cu = 0;
 };
 bool route_single_writer(int t_r);                    // (query, document) scores have one writer
 bool route_use_wide(int dtype, int h_r, int d_r, int t_r);     // GEMM-tiled scan for many rows per query

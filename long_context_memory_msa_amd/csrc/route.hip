@@ -389,7 +389,12 @@ hipError_t route_launch(const RouteArgs &a, hipStream_t s) {
   const int64_t n_tiles = (a.n_chunks + 15) / 16;
   const int n_rows = a.n_q * a.t_r;
   const int rbs = (n_rows + 15) / 16;
-  const int64_t slots = (int64_t)device_cu_count() * resident;  // resident workgroups
+  // a caller that runs other kernels beside the scan (a pipelined decode step)
+  // caps the workgroups per compute unit: while every compute unit holds more
+  // than one of the scan's persistent workgroups, kernels on other streams
+  // wait for the scan's waves to retire
+  const int per_cu = a.max_wg_per_cu > 0 && a.max_wg_per_cu < resident ? a.max_wg_per_cu : resident;
+  const int64_t slots = (int64_t)device_cu_count() * per_cu;  // resident workgroups
   int64_t wgs = std::max<int64_t>(1, slots / rbs);
   wgs = std::min<int64_t>(wgs, (n_tiles + 3) / 4);
 #if MSA_ROUTE_BALANCE

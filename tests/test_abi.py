@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_empty_error():
-    assert msa.msa_abi_version() == 2
+    assert msa.msa_abi_version() == 3
     msa.msa_bank_layout([3], 2)
     assert msa.msa_last_error() == ""
 
@@ -145,6 +145,8 @@ def test_route_validation():
     assert _code(msa.msa_route_score, _bank(), A, 1, 0, A, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
     assert _code(msa.msa_route_score, _bank(), MIS, 1, 1, A, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
     assert _code(msa.msa_route_score, _bank(), A, 1, 1, None, None, A, 1 << 30, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_route_score, _bank(), A, 1, 1, A, None, A, 1 << 30, stream=0,
+                 max_wg_per_cu=-1) == L.MSA_ERR_ARG
 
 
 def test_topk_validation_and_workspace():

@@ -139,6 +139,13 @@ def test_route_isolated(device, name, t_r, n_q):
     L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc2, None, ws, nb)
     torch.cuda.synchronize()
     assert torch.equal(s_doc, s_doc2)
+    # a persistent grid capped at 1 or 2 workgroups per compute unit: the
+    # same tiles, other waves -- identical scores
+    for cap in (1, 2):
+        s_doc3, s_chunk3 = torch.empty_like(s_doc), torch.empty_like(s_chunk)
+        L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc3, s_chunk3, ws, nb, max_wg_per_cu=cap)
+        torch.cuda.synchronize()
+        assert torch.equal(s_doc, s_doc3) and torch.equal(s_chunk, s_chunk3), cap
 
 
 # every router head shape the ABI admits (h_r in 1..16, d_r 64 / 128 / 256 --

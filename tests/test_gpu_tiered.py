@@ -86,3 +86,25 @@ def test_decode_pipeline_equals_layer_forward(device, kv_host):
             assert torch.equal(pipe.idx[s], idx) and torch.equal(pipe.val[s], val)
             assert torch.equal(pipe.s_doc[s], s_doc)
             assert torch.equal(pipe.O[s], O_)
+
+
+@pytest.mark.parametrize("route_streams,slots,cap", [(1, 3, 0), (2, 3, 1), (3, 4, 1), (2, 4, 2)])
+def test_decode_pipeline_streams_and_slots(device, route_streams, slots, cap):
+    # more steps in flight than slots (the host waits before reusing one), the
+    # scans spread over 1-3 route streams with full or capped grids: the
+    # steps whose slots were not reused equal the layer forward
+    w = W.make_workload(3, bank_tokens=700_000)
+    log(f"pipeline streams={route_streams} slots={slots} cap={cap}: chunks={w.n_chunks}")
+    qi0, K, V, KR = host_inputs(w)
+    bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
+    n_steps = slots + 2
+    batches = [query_views(w, W.query_inputs(w, layer), device) for layer in range(n_steps)]
+    pipe = DecodePipeline(bank, rope, w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k, w.pos0, device=device,
+                          slots=slots, route_streams=route_streams, max_wg_per_cu=cap)
+    got = [pipe.step(*b) for b in batches]
+    pipe.synchronize()
+    for i in range(n_steps - slots, n_steps):
+        O_, idx, val, s_doc = run_layer(bank, rope, w, *batches[i], device)
+        s = got[i]
+        assert torch.equal(pipe.idx[s], idx) and torch.equal(pipe.val[s], val), i
+        assert torch.equal(pipe.s_doc[s], s_doc) and torch.equal(pipe.O[s], O_), i
