@@ -180,7 +180,7 @@ def bench_interleave(args) -> int:
     from long_context_memory_msa_amd import _lib as L, memory as M, offline
 
     dev = torch.device("cuda:0")
-    w = W.make_workload(4)
+    w = W.make_workload("interleave-10mx18")
     print(f"[bench] {w.name}: {w.n_layers} layers x {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks",
           file=sys.stderr, flush=True)
     banks, layers = [], []
@@ -318,7 +318,7 @@ def bench_append(args) -> int:
     from long_context_memory_msa_amd import _lib as L, memory as M, offline
 
     dev = torch.device("cuda:0")
-    w = W.make_workload(3, bank_tokens=args.bank_tokens)
+    w = W.make_workload("decode-100m", bank_tokens=args.bank_tokens)
     qi = W.query_inputs(w)
     uhat = torch.from_numpy(W.gold_uhat(w, qi["QR"])).to(dev)
     td = M.TORCH_DTYPE[w.dtype]
@@ -395,7 +395,7 @@ def bench_tiered(args) -> int:
     from long_context_memory_msa_amd.pipeline import DecodePipeline
 
     dev = torch.device("cuda:0")
-    w = W.make_workload(3, bank_tokens=args.bank_tokens)
+    w = W.make_workload("decode-100m", bank_tokens=args.bank_tokens)
     print(f"[bench] tiered {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr,
           flush=True)
     qi = W.query_inputs(w)
@@ -525,7 +525,7 @@ def main() -> int:
         return bench_append(args)
     if args.workload == "project":
         return bench_project(args)
-    w = W.make_workload(3, bank_tokens=args.bank_tokens)
+    w = W.make_workload("decode-100m", bank_tokens=args.bank_tokens)
     print(f"[bench] {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr, flush=True)
 
     # ---- queries (host-generated, uploaded) and the pooled bank (device) -------

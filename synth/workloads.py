@@ -127,50 +127,56 @@ def _gold(seed: int, n_docs: int, n_q: int, n_gold: int) -> np.ndarray:
     return np.sort(pick.reshape(n_q, n_gold), axis=1).astype(np.int64)
 
 
-def make_workload(cfg: int, seed: Optional[int] = None, bank_tokens: Optional[int] = None,
-                  n_layers: Optional[int] = None, n_q: Optional[int] = None) -> Workload:
-    """Workload ``cfg`` (0..4); ``bank_tokens`` / ``n_layers`` / ``n_q`` shrink it.
+# the five workloads by name; the number is each one's default seed
+WORKLOADS = {"tiny-f32": 0, "prefill-16k": 1, "prefill-1m": 2, "decode-100m": 3, "interleave-10mx18": 4}
 
-    0: tiny fp32 layer, 64 docs x 512 tokens, chunk 64, 2 router / 2 KV / 4 q
-       heads of dim 64, 16 query tokens, k=4, 4 gold docs.
-    1: 16K-token bank, 32 docs x 512, chunk 128, 8 router heads x 128, 32 q / 8
-       KV heads x 128, bf16, 128 causal query tokens, k=8, 4 gold docs.
-    2: 1M-token bank, doc lengths U[256,4096], 256 query tokens, k=16, 8 gold.
-    3: 100M-token bank, doc lengths U[512,8192], 16 queries x 1 decode token,
-       k=16, 8 gold docs per query (distinct across queries).
-    4: 10M-token bank per layer x 18 routed layers, U[256,4096], prefill 512,
-       3 interleave rounds appending 64 tokens, k=8, no gold.
+
+def make_workload(name: str, seed: Optional[int] = None, bank_tokens: Optional[int] = None,
+                  n_layers: Optional[int] = None, n_q: Optional[int] = None) -> Workload:
+    """Workload ``name``; ``bank_tokens`` / ``n_layers`` / ``n_q`` shrink it.
+
+    tiny-f32: fp32 layer, 64 docs x 512 tokens, chunk 64, 2 router / 2 KV /
+       4 q heads of dim 64, 16 query tokens, k=4, 4 gold docs.
+    prefill-16k: 16K-token bank, 32 docs x 512, chunk 128, 8 router heads x
+       128, 32 q / 8 KV heads x 128, bf16, 128 causal query tokens, k=8, 4 gold.
+    prefill-1m: 1M-token bank, doc lengths U[256,4096], 256 query tokens, k=16,
+       8 gold.
+    decode-100m: 100M-token bank, doc lengths U[512,8192], 16 queries x 1
+       decode token, k=16, 8 gold docs per query (distinct across queries).
+    interleave-10mx18: 10M-token bank per layer x 18 routed layers,
+       U[256,4096], prefill 512, 3 interleave rounds appending 64 tokens, k=8,
+       no gold.
     """
-    s = cfg if seed is None else seed
-    if cfg == 0:
+    if name not in WORKLOADS:
+        raise ValueError(f"unknown workload {name!r}; one of {sorted(WORKLOADS)}")
+    s = WORKLOADS[name] if seed is None else seed
+    if name == "tiny-f32":
         total = bank_tokens or 64 * 512
         lens = np.full(total // 512, 512, dtype=np.int64) if total % 512 == 0 else _doc_lengths(s, total, 512, 512)
-        w = Workload("cfg0-tiny-fp32", "f32", lens, 64, 2, 64, 2, 64, 4, n_q or 1, 16, 16, 16, 4, 4,
+        w = Workload(name, "f32", lens, 64, 2, 64, 2, 64, 4, n_q or 1, 16, 16, 16, 4, 4,
                      np.zeros((0, 0), np.int64), s)
         n_gold = 4
-    elif cfg == 1:
+    elif name == "prefill-16k":
         total = bank_tokens or 32 * 512
         lens = np.full(total // 512, 512, dtype=np.int64) if total % 512 == 0 else _doc_lengths(s, total, 512, 512)
-        w = Workload("cfg1-16K-bf16", "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 1, 128, 128, 128, 8, 8,
+        w = Workload(name, "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 1, 128, 128, 128, 8, 8,
                      np.zeros((0, 0), np.int64), s)
         n_gold = 4
-    elif cfg == 2:
+    elif name == "prefill-1m":
         lens = _doc_lengths(s, bank_tokens or 1_000_000, 256, 4096)
-        w = Workload("cfg2-1M-bf16", "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 1, 256, 256, 256, 16, 16,
+        w = Workload(name, "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 1, 256, 256, 256, 16, 16,
                      np.zeros((0, 0), np.int64), s)
         n_gold = 8
-    elif cfg == 3:
+    elif name == "decode-100m":
         lens = _doc_lengths(s, bank_tokens or 100_000_000, 512, 8192)
-        w = Workload("cfg3-100M-decode", "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 16, 1, 1, 1, 16, 16,
+        w = Workload(name, "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 16, 1, 1, 1, 16, 16,
                      np.zeros((0, 0), np.int64), s)
         n_gold = 8
-    elif cfg == 4:
+    else:  # interleave-10mx18
         lens = _doc_lengths(s, bank_tokens or 10_000_000, 256, 4096)
-        w = Workload("cfg4-10Mx18-interleave", "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 1, 512, 512, 512,
+        w = Workload(name, "bf16", lens, 128, 8, 128, 8, 128, 32, n_q or 1, 512, 512, 512,
                      8, 8, np.zeros((0, 0), np.int64), s, n_layers=n_layers or 18, rounds=3, append=64)
         n_gold = 0
-    else:
-        raise ValueError(cfg)
     n_gold = min(n_gold, w.n_docs // max(1, w.n_q))
     w.gold = _gold(s, w.n_docs, w.n_q, n_gold)
     return w

@@ -1,14 +1,14 @@
 """GPU parity at the workloads' full sizes, in the launch configuration bench.py
 times.
 
-* 1M-token bank (config 2): the whole layer against the oracle.
-* 100M-token bank (config 3, decode): the bank is generated and pooled on the
+* 1M-token bank (prefill-1m): the whole layer against the oracle.
+* 100M-token bank (decode-100m): the bank is generated and pooled on the
   GPU slab by slab; the oracle regenerates a sample of documents (first, last,
   gold, random; >= 4096 chunks) from the same counter generator and checks
   their pooled rows and router scores; top-k is checked by its defining
   property on the GPU's own scores plus planted-gold recovery; attention runs
   at full size on test-chosen documents and is checked for sampled queries.
-* 18 routed layers x 10M tokens with 3 Memory Interleave rounds (config 4):
+* 18 routed layers x 10M tokens with 3 Memory Interleave rounds (interleave-10mx18):
   per-layer banks on the GPU, the interleave driver, sampled pooled rows and
   router scores for sampled layers and rounds, top-k properties everywhere,
   and full-shape attention (prefill and a later round) against the oracle.
@@ -97,7 +97,7 @@ def compact_bank(ob_docs, docs):
 
 # ---------------------------------------------------------------------------
 def test_full_1m_bank_layer(device):
-    w = W.make_workload(2)
+    w = W.make_workload("prefill-1m")
     log(f"1M bank: {w.n_docs} docs, {w.n_chunks} chunks")
     qi = W.query_inputs(w)
     uh = W.gold_uhat(w, qi["QR"])
@@ -136,7 +136,7 @@ def test_full_1m_bank_layer(device):
 
 # ---------------------------------------------------------------------------
 def test_full_100m_bank_decode(device):
-    w = W.make_workload(3)
+    w = W.make_workload("decode-100m")
     log(f"100M bank: {w.n_docs} docs, {w.n_chunks} chunks")
     qi = W.query_inputs(w)
     uh = W.gold_uhat(w, qi["QR"])
@@ -198,7 +198,7 @@ def test_full_100m_bank_decode(device):
 
 # ---------------------------------------------------------------------------
 def test_full_interleave_18_layers(device):
-    w = W.make_workload(4)
+    w = W.make_workload("interleave-10mx18")
     log(f"interleave: {w.n_layers} layers x {w.n_docs} docs, {w.n_chunks} chunks, {w.rounds} rounds")
     banks, layers, hosts = [], [], []
     for layer in range(w.n_layers):

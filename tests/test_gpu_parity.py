@@ -35,18 +35,18 @@ def device():
     return torch.device("cuda:0")
 
 
-def _wl(cfg, bank_tokens=None, **kw):
-    w = W.make_workload(cfg, bank_tokens=bank_tokens)
+def _wl(name, bank_tokens=None, **kw):
+    w = W.make_workload(name, bank_tokens=bank_tokens)
     return dataclasses.replace(w, **kw) if kw else w
 
 
-# small versions of the five workloads: (config, bank tokens) -- ragged where the law allows
+# small versions of the five workloads: (workload, bank tokens) -- ragged where the law allows
 SMALL = {
-    "cfg0": (0, None),
-    "cfg1": (1, None),
-    "cfg2": (2, 150_000),
-    "cfg3": (3, 700_000),
-    "cfg4": (4, 120_000),
+    "tiny": ("tiny-f32", None),
+    "16k": ("prefill-16k", None),
+    "1m": ("prefill-1m", 150_000),
+    "decode": ("decode-100m", 700_000),
+    "interleave": ("interleave-10mx18", 120_000),
 }
 
 
@@ -84,10 +84,10 @@ def _check_pool(w, ob, bank):
     assert np.array_equal(bank.chunk_doc.cpu().numpy(), ob["chunk_doc"])
 
 
-@pytest.mark.parametrize("name,n_slabs", [("cfg0", 1), ("cfg1", 2), ("cfg2", 3), ("cfg4", 1)])
+@pytest.mark.parametrize("name,n_slabs", [("tiny", 1), ("16k", 2), ("1m", 3), ("interleave", 1)])
 def test_pool(device, name, n_slabs):
-    cfg, bt = SMALL[name]
-    w = _wl(cfg, bt)
+    wname, bt = SMALL[name]
+    w = _wl(wname, bt)
     log(f"pool {name} docs={w.n_docs} chunks={w.n_chunks} slabs={n_slabs}")
     qi, K, V, KR = host_inputs(w)
     ob = oracle_bank(w, K, V, KR)
@@ -98,7 +98,7 @@ def test_pool(device, name, n_slabs):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_pool_edge_lengths(device, dtype):
     # lengths around the chunk size, single-token documents, one long document
-    base = _wl(0) if dtype == "f32" else _wl(1)
+    base = _wl("tiny-f32") if dtype == "f32" else _wl("prefill-16k")
     C = base.chunk
     lens = np.array([1, C - 1, C, C + 1, 3 * C + 5, 2, C // 2, 7 * C], dtype=np.int64)
     w = dataclasses.replace(base, doc_lens=lens, gold=np.zeros((1, 0), np.int64))
@@ -110,13 +110,13 @@ def test_pool_edge_lengths(device, dtype):
 
 
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name,t_r,n_q", [("cfg0", 16, 1), ("cfg1", 128, 1), ("cfg1", 1, 1), ("cfg1", 5, 3),
-                                          ("cfg1", 40, 2), ("cfg1", 16, 3), ("cfg1", 1, 37), ("cfg1", 48, 3),
-                                          ("cfg1", 64, 5), ("cfg2", 256, 1),
-                                          ("cfg3", 1, 16)])
+@pytest.mark.parametrize("name,t_r,n_q", [("tiny", 16, 1), ("16k", 128, 1), ("16k", 1, 1), ("16k", 5, 3),
+                                          ("16k", 40, 2), ("16k", 16, 3), ("16k", 1, 37), ("16k", 48, 3),
+                                          ("16k", 64, 5), ("1m", 256, 1),
+                                          ("decode", 1, 16)])
 def test_route_isolated(device, name, t_r, n_q):
-    cfg, bt = SMALL[name]
-    w = _wl(cfg, bt)
+    wname, bt = SMALL[name]
+    w = _wl(wname, bt)
     if n_q != w.n_q:
         w = dataclasses.replace(w, n_q=n_q, gold=np.zeros((n_q, 0), np.int64))
     log(f"route {name} t_r={t_r} n_q={n_q} chunks={w.n_chunks}")
@@ -158,7 +158,7 @@ def test_route_isolated(device, name, t_r, n_q):
     ("f32", 4, 128, 5, 2), ("f32", 8, 128, 48, 1),
     ("bf16", 4, 256, 1, 16), ("bf16", 2, 256, 48, 2), ("bf16", 1, 256, 16, 3)])
 def test_route_head_shapes(device, dtype, h_r, d_r, t_r, n_q):
-    w = _wl(2, 60_000)
+    w = _wl("prefill-1m", 60_000)
     # one small attention head: K/V do not enter the routing
     w = dataclasses.replace(w, dtype=dtype, h_r=h_r, d_r=d_r, h_kv=1, d=64, h_q=1, n_q=n_q,
                             gold=np.zeros((n_q, 0), np.int64))
@@ -223,10 +223,10 @@ def _attend_case(w, device, idx_h, T=None, L_loc=None):
     return host(out), want
 
 
-@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2", "cfg3"])
+@pytest.mark.parametrize("name", ["tiny", "16k", "1m", "decode"])
 def test_attend_isolated(device, name):
-    cfg, bt = SMALL[name]
-    w = _wl(cfg, bt)
+    wname, bt = SMALL[name]
+    w = _wl(wname, bt)
     g = np.random.default_rng(7)
     idx_h = np.stack([g.choice(w.n_docs, size=w.k, replace=False) for _ in range(w.n_q)])
     log(f"attend {name} n_q={w.n_q} T={w.T} L_loc={w.L_loc} k={w.k}")
@@ -237,7 +237,7 @@ def test_attend_isolated(device, name):
 
 def test_attend_all_documents_is_dense(device):
     # k = n_docs: attention over the whole compressed memory plus the local context
-    w = _wl(0)
+    w = _wl("tiny-f32")
     idx_h = np.random.default_rng(3).permutation(w.n_docs)[None, :]
     w = dataclasses.replace(w, k=w.n_docs, pos0=w.n_docs)
     got, want = _attend_case(w, device, idx_h)
@@ -247,7 +247,7 @@ def test_attend_all_documents_is_dense(device):
 @pytest.mark.parametrize("T,L_loc", [(1, 1), (1, 37), (3, 70), (50, 50), (64, 640)])
 def test_attend_shapes(device, T, L_loc):
     # decode and partial prefill over long local contexts (causal tails, several key tiles)
-    w = _wl(1)
+    w = _wl("prefill-16k")
     w = dataclasses.replace(w, T=T, L_loc=L_loc, T_route=min(L_loc, 128), rounds=1, append=0)
     idx_h = np.random.default_rng(T + L_loc).choice(w.n_docs, size=(1, w.k), replace=False)
     got, want = _attend_case(w, device, idx_h, T, L_loc)
@@ -255,10 +255,10 @@ def test_attend_shapes(device, T, L_loc):
 
 
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2", "cfg3"])
+@pytest.mark.parametrize("name", ["tiny", "16k", "1m", "decode"])
 def test_layer_end_to_end(device, name):
-    cfg, bt = SMALL[name]
-    w = _wl(cfg, bt)
+    wname, bt = SMALL[name]
+    w = _wl(wname, bt)
     log(f"layer {name} docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q} T={w.T}")
     qi, K, V, KR = host_inputs(w)
     ob = oracle_bank(w, K, V, KR)
@@ -291,8 +291,8 @@ def test_bank_append_equals_one_pass_encoding(device):
     # capacity, routed (checked against the oracle on that half), then the
     # rest appended and pooled in place -- the result equals the bank encoded
     # in one pass, value for value, and so does the layer over it
-    cfg, bt = SMALL["cfg2"]
-    w = _wl(cfg, bt)
+    wname, bt = SMALL["1m"]
+    w = _wl(wname, bt)
     qi, K, V, KR = host_inputs(w)
     full, rope = gpu_bank_pooled(w, K, V, KR, device, 2)
     half = w.n_docs // 2
@@ -330,7 +330,7 @@ def test_bank_append_equals_one_pass_encoding(device):
 
 
 def test_layer_equals_composition_and_is_deterministic(device):
-    w = _wl(3, 300_000)
+    w = _wl("decode-100m", 300_000)
     qi, K, V, KR = host_inputs(w)
     bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
     QR, Q, Kl, Vl = query_views(w, qi, device)
@@ -378,12 +378,12 @@ def _layer_halves(bank, rope, w, QR, Q, Kl, Vl, device):
 
 
 # the halves against the whole layer: single-writer scan with single-pass top-k
-# (cfg3 small), many-row tiled scan (cfg1, 128 router rows), atomic keys
-# (cfg1, 5 router rows), and the fp32 decode scan (cfg0)
-@pytest.mark.parametrize("name,t_r", [("cfg3", 1), ("cfg1", 128), ("cfg1", 5), ("cfg0", 16)])
+# (decode small), many-row tiled scan (16k, 128 router rows), atomic keys
+# (16k, 5 router rows), and the fp32 decode scan (tiny)
+@pytest.mark.parametrize("name,t_r", [("decode", 1), ("16k", 128), ("16k", 5), ("tiny", 16)])
 def test_layer_halves_equal_layer_forward(device, name, t_r):
-    cfg, bt = SMALL[name]
-    w = _wl(cfg, bt, T_route=t_r)
+    wname, bt = SMALL[name]
+    w = _wl(wname, bt, T_route=t_r)
     log(f"layer halves {name} t_r={t_r} docs={w.n_docs}")
     qi, K, V, KR = host_inputs(w)
     bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
@@ -402,7 +402,7 @@ def test_layer_sliced_topk_selected_in_attention(device, k):
     # separate route / top-k / attend calls bit for bit, and the oracle
     g = np.random.default_rng(11)
     lens = g.integers(8, 41, size=9_000).astype(np.int64)  # one chunk per document
-    w = _wl(3, 200_000, doc_lens=lens, chunk=64, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, n_q=4, k=k, pos0=k,
+    w = _wl("decode-100m", 200_000, doc_lens=lens, chunk=64, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, n_q=4, k=k, pos0=k,
             gold=np.zeros((4, 0), dtype=np.int64))
     assert w.n_docs > 8192 and w.n_chunks == w.n_docs
     log(f"sliced layer k={k}: docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q}")
@@ -453,7 +453,7 @@ def test_layer_sliced_topk_selected_in_attention(device, k):
 def test_layer_degenerate_banks(device, lens, k, t_r):
     lens = np.asarray(lens, dtype=np.int64)
     n_q = 2
-    w = _wl(1, None, doc_lens=lens, k=k, pos0=k, n_q=n_q, T=8, L_loc=max(32, t_r), T_route=t_r,
+    w = _wl("prefill-16k", None, doc_lens=lens, k=k, pos0=k, n_q=n_q, T=8, L_loc=max(32, t_r), T_route=t_r,
             gold=np.zeros((n_q, 0), np.int64))
     log(f"degenerate bank lens={lens.tolist()} k={k} t_r={t_r} chunks={w.n_chunks}")
     qi, K, V, KR = host_inputs(w)
@@ -474,7 +474,7 @@ def test_layer_degenerate_banks(device, lens, k, t_r):
 def test_scan_read_probe_runs(device):
     # the bandwidth probe reads the bank in the scan's pattern and writes one
     # finite record per 16-chunk tile (its values carry no meaning)
-    w = _wl(3, 700_000)
+    w = _wl("decode-100m", 700_000)
     qi, K, V, KR = host_inputs(w)
     bank, _ = gpu_bank_pooled(w, K, V, KR, device, 1)
     n_tiles = (w.n_chunks + 15) // 16
@@ -488,7 +488,7 @@ def test_interleave_small(device):
     # the interleave driver on 2 layers of a small bank against the oracle's loop
     from long_context_memory_msa_amd.interleave import interleave
 
-    w = W.make_workload(4, bank_tokens=120_000, n_layers=2)
+    w = W.make_workload("interleave-10mx18", bank_tokens=120_000, n_layers=2)
     banks, layers, ob_banks, hosts = [], [], [], []
     for layer in range(w.n_layers):
         qi = W.query_inputs(w, layer)

@@ -65,7 +65,7 @@ def test_project_isolated(device, rows, hidden, out):
 def test_projected_route_router_twice_head_width(device):
     # memory-token hidden states -> K^R per token -> pooled bank with h_r = 4 x d_r = 256;
     # query hidden states -> Q^R; route and document reduction against the oracle
-    w = W.make_workload(1)                      # 32 documents x 512 tokens, chunk 128, bf16
+    w = W.make_workload("prefill-16k")                      # 32 documents x 512 tokens, chunk 128, bf16
     hidden, h_r, d_r, t_r = 640, 4, 256, 48
     n_q = 2
     log(f"projected route: {w.n_tok} tokens, hidden={hidden}, router {h_r} x {d_r}, t_r={t_r}")

@@ -43,7 +43,7 @@ def test_device_pointer_rejects_unpinned():
 
 
 def test_tiered_bank_equals_hbm_bank(device):
-    w = W.make_workload(2, bank_tokens=150_000)
+    w = W.make_workload("prefill-1m", bank_tokens=150_000)
     log(f"tiered layer: docs={w.n_docs} chunks={w.n_chunks}")
     qi, K, V, KR = host_inputs(w)
     ref, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
@@ -70,7 +70,7 @@ def test_tiered_bank_equals_hbm_bank(device):
 def test_decode_pipeline_equals_layer_forward(device, kv_host):
     # four independent query batches (the seeded query inputs of four layers)
     # through the two-stream pipeline, two steps in flight at a time
-    w = W.make_workload(3, bank_tokens=700_000)
+    w = W.make_workload("decode-100m", bank_tokens=700_000)
     log(f"pipeline kv_host={kv_host}: docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q}")
     qi0, K, V, KR = host_inputs(w)
     ref, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
@@ -93,7 +93,7 @@ def test_decode_pipeline_streams_and_slots(device, route_streams, slots, cap):
     # more steps in flight than slots (the host waits before reusing one), the
     # scans spread over 1-3 route streams with full or capped grids: the
     # steps whose slots were not reused equal the layer forward
-    w = W.make_workload(3, bank_tokens=700_000)
+    w = W.make_workload("decode-100m", bank_tokens=700_000)
     log(f"pipeline streams={route_streams} slots={slots} cap={cap}: chunks={w.n_chunks}")
     qi0, K, V, KR = host_inputs(w)
     bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)

@@ -330,9 +330,9 @@ def _oracle_layer(w):
     return res
 
 
-@pytest.mark.parametrize("cfg", [0, 1])
-def test_planted_gold_recovered(cfg):
-    w = W.make_workload(cfg)
+@pytest.mark.parametrize("name", ["tiny-f32", "prefill-16k"])
+def test_planted_gold_recovered(name):
+    w = W.make_workload(name)
     res = _oracle_layer(w)
     for q in range(w.n_q):
         assert set(w.gold[q].tolist()) <= set(res["idx"][q].tolist())
@@ -341,7 +341,7 @@ def test_planted_gold_recovered(cfg):
 @pytest.mark.slow
 def test_planted_gold_recovered_decode_shape():
     # the 100M-token decode workload's shape (16 queries x 1 token, k=16, 8 gold each) on a 2M-token bank
-    w = W.make_workload(3, bank_tokens=2_000_000)
+    w = W.make_workload("decode-100m", bank_tokens=2_000_000)
     res = _oracle_layer(w)
     for q in range(w.n_q):
         assert set(w.gold[q].tolist()) <= set(res["idx"][q].tolist())
