@@ -52,7 +52,7 @@ enum {
 
 enum { MSA_F32 = 0, MSA_BF16 = 1 };
 
-/* RoPE cos/sin tables, fp32 [max_pos][d/2] each (see msa_rope_table). */
+/* RoPE cos/sin tables, fp32 [max_pos][d/2] each, 16-byte aligned (see msa_rope_table). */
 typedef struct msa_rope {
   const float *cos;
   const float *sin;

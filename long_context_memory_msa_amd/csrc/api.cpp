@@ -81,8 +81,8 @@ int check_bank(const msa_bank *b) {
 
 int check_rope(const msa_rope *r, int d, int64_t need_pos) {
   if (!r) return fail(MSA_ERR_ARG, "rope is null");
-  CHECK_PTR(r->cos, 4, "rope.cos");
-  CHECK_PTR(r->sin, 4, "rope.sin");
+  CHECK_PTR(r->cos, 16, "rope.cos");
+  CHECK_PTR(r->sin, 16, "rope.sin");
   if (r->d != d) return fail(MSA_ERR_ARG, "rope.d = %d but head dim is %d", r->d, d);
   if ((int64_t)r->max_pos < need_pos)
     return fail(MSA_ERR_ARG, "rope.max_pos = %d < %lld positions needed", r->max_pos, (long long)need_pos);
@@ -411,8 +411,8 @@ int msa_bank_layout(const int64_t *doc_lens, int32_t n_docs, int32_t chunk, int6
 
 int msa_rope_table(float *cos, float *sin, int32_t max_pos, int32_t d, double base, void *stream) {
   try {
-    CHECK_PTR(cos, 4, "cos");
-    CHECK_PTR(sin, 4, "sin");
+    CHECK_PTR(cos, 16, "cos");
+    CHECK_PTR(sin, 16, "sin");
     if (max_pos < 1) return fail(MSA_ERR_ARG, "max_pos = %d", max_pos);
     if (d != 64 && d != 128) return fail(MSA_ERR_UNSUPPORTED, "d = %d (64 or 128)", d);
     if (!(base > 0.0) || !std::isfinite(base)) return fail(MSA_ERR_ARG, "base must be finite and > 0");

@@ -8,10 +8,19 @@
 //
 // Memory-bound: each chunk reads C * (2 h_kv d + h_r d_r) elements once and
 // writes (2 h_kv d + h_r d_r) elements plus h_r norms.  One workgroup per
-// chunk; each wave reduces whole head rows of one tensor, 16-byte loads, the
-// tokens of a chunk spread over the wave's token groups.
+// chunk.  bf16 banks whose token rows are whole 1 KB pieces (h_kv d and h_r d_r
+// multiples of 512): one wave per piece of the K, V and K^R rows, lane l owning
+// elements 8l..8l+7 of the piece for every token of the chunk -- each load
+// instruction reads 1 KB of one token row, and no cross-lane sum is needed.
+// Other shapes: each wave reduces whole head rows of one tensor, 16-byte
+// loads, the tokens of a chunk spread over the wave's token groups.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
+
+// 1 = the bf16 piece-wise pooling kernel where the shapes allow it
+#ifndef MSA_POOL_PIECES
+#define MSA_POOL_PIECES 1
+#endif
 
 namespace msa {
 namespace {
@@ -149,6 +158,116 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   }
 }
 
+// bf16, one wave per 1 KB piece of a token row (512 elements): pieces
+// [0, PK) of K, [PK, 2 PK) of V, [2 PK, 2 PK + PR) of K^R.
+template <int D, int DR>
+__global__ __launch_bounds__(1024) void pool_pieces_kernel(PoolArgs a) {
+  constexpr int XL = D / 16;  // lanes between RoPE partners (elements e and e + D/2)
+  const int64_t c = a.chunk_begin + blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int piece = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int doc = a.chunk_doc[c];
+  const int64_t dtok = a.doc_tok_off[doc];
+  const int64_t L = a.doc_tok_off[doc + 1] - dtok;
+  const int64_t j0 = (c - a.doc_chunk_off[doc]) * a.chunk;  // in-document start
+  const int n_tok = (int)min((int64_t)a.chunk, L - j0);
+  const int64_t row0 = dtok + j0 - a.slab_tok0;
+  const int PK = a.h_kv * D / 512;
+  const int kind = piece < PK ? 0 : (piece < 2 * PK ? 1 : 2);  // K, V, K^R
+  const int pi = kind == 2 ? piece - 2 * PK : piece - kind * PK;
+  const int rowlen = kind == 2 ? a.h_r * DR : a.h_kv * D;     // elements per token row
+  const int e = pi * 512 + lane * 8;                          // this lane's first element in the row
+  const bf16_t *src = static_cast<const bf16_t *>(kind == 0 ? a.K : (kind == 1 ? a.V : a.KR)) + row0 * rowlen + e;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  if (kind == 0) {
+    // document-wise RoPE at in-document positions j0 + t (rotate-half pairs)
+    const int ei = e % D;
+    const bool lo = ei < D / 2;
+    const float *cp = a.cos + j0 * (D / 2) + ei % (D / 2);
+    const float *sp = a.sin + j0 * (D / 2) + ei % (D / 2);
+#pragma unroll 4
+    for (int t = 0; t < n_tok; ++t) {
+      const uint4 raw = *reinterpret_cast<const uint4 *>(src + (int64_t)t * rowlen);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      const float4 c0 = *reinterpret_cast<const float4 *>(cp + t * (D / 2));
+      const float4 c1 = *reinterpret_cast<const float4 *>(cp + t * (D / 2) + 4);
+      const float4 s0 = *reinterpret_cast<const float4 *>(sp + t * (D / 2));
+      const float4 s1 = *reinterpret_cast<const float4 *>(sp + t * (D / 2) + 4);
+      const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = __uint_as_float(w[j] << 16), x1 = __uint_as_float(w[j] & 0xFFFF0000u);
+        const float p0 = __shfl_xor(x0, XL, 64), p1 = __shfl_xor(x1, XL, 64);
+        acc[2 * j] += lo ? (x0 * cs[2 * j] - p0 * sn[2 * j]) : (p0 * sn[2 * j] + x0 * cs[2 * j]);
+        acc[2 * j + 1] += lo ? (x1 * cs[2 * j + 1] - p1 * sn[2 * j + 1]) : (p1 * sn[2 * j + 1] + x1 * cs[2 * j + 1]);
+      }
+    }
+  } else {
+#pragma unroll 8
+    for (int t = 0; t < n_tok; ++t) {
+      const uint4 raw = *reinterpret_cast<const uint4 *>(src + (int64_t)t * rowlen);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(w[j] << 16);
+        acc[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+  }
+  // chunk mean, rounded once to bf16 (RNE); 16 bytes per lane
+  const float cnt = (float)n_tok;
+  float r[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    r[j] = Elem<bf16_t>::round(acc[j] / cnt);
+    ss += r[j] * r[j];
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = (__float_as_uint(r[2 * j]) >> 16) | (__float_as_uint(r[2 * j + 1]) & 0xFFFF0000u);
+  const uint4 ov{o[0], o[1], o[2], o[3]};
+  if (kind == 2) {
+    const int h = e / DR, eh = e % DR;
+    *reinterpret_cast<uint4 *>(static_cast<bf16_t *>(a.krbar) + (c * a.h_r + h) * DR + eh) = ov;
+    // 1/||stored row|| over the DR / 8 lanes of head h
+#pragma unroll
+    for (int m = 1; m < DR / 8; m <<= 1) ss += __shfl_xor(ss, m, 64);
+    if (eh == 0) a.kr_inv_norm[c * a.h_r + h] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.0f;
+  } else {
+    const int h = e / D, eh = e % D;
+    bf16_t *dst = static_cast<bf16_t *>(kind == 0 ? a.kbar : a.vbar);
+    *reinterpret_cast<uint4 *>(dst + ((int64_t)h * a.kv_stride + c) * D + eh) = ov;
+  }
+}
+
+bool pool_pieces_ok(const PoolArgs &a) {
+  return a.dtype == 1 && (a.h_kv * a.d) % 512 == 0 && (a.h_r * a.d_r) % 512 == 0 &&
+         2 * (a.h_kv * a.d / 512) + a.h_r * a.d_r / 512 <= 16;
+}
+
+template <int D, int DR>
+hipError_t pool_pieces_launch(const PoolArgs &a, hipStream_t s) {
+  const int pieces = 2 * (a.h_kv * D / 512) + a.h_r * DR / 512;
+  hipLaunchKernelGGL((pool_pieces_kernel<D, DR>), dim3((unsigned)(a.chunk_end - a.chunk_begin)), dim3(64 * pieces), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+hipError_t pool_pieces_dispatch(const PoolArgs &a, hipStream_t s) {
+  if (a.d == 64) {
+    if (a.d_r == 64) return pool_pieces_launch<64, 64>(a, s);
+    if (a.d_r == 128) return pool_pieces_launch<64, 128>(a, s);
+    return pool_pieces_launch<64, 256>(a, s);
+  }
+  if (a.d_r == 64) return pool_pieces_launch<128, 64>(a, s);
+  if (a.d_r == 128) return pool_pieces_launch<128, 128>(a, s);
+  return pool_pieces_launch<128, 256>(a, s);
+}
+
 template <typename T>
 hipError_t pool_dispatch(const PoolArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.chunk_end - a.chunk_begin)), block(256);
@@ -182,6 +301,7 @@ hipError_t launch_pool(const PoolArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.chunk_end <= a.chunk_begin) return hipSuccess;
+  if (MSA_POOL_PIECES && pool_pieces_ok(a)) return pool_pieces_dispatch(a, s);
   return a.dtype == 0 ? pool_dispatch<float>(a, s) : pool_dispatch<bf16_t>(a, s);
 }
 

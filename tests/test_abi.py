@@ -239,3 +239,14 @@ def test_scan_read_probe_validation():
     assert _code(msa.msa_scan_read_probe, b, None, need, stream=0) == L.MSA_ERR_WORKSPACE
     assert _code(msa.msa_scan_read_probe, _bank(dtype=L.MSA_F32), A, need, stream=0) == L.MSA_ERR_UNSUPPORTED
     assert _code(msa.msa_scan_read_probe, _bank(h_r=4), A, need, stream=0) == L.MSA_ERR_UNSUPPORTED
+
+
+def test_rope_tables_must_be_16_byte_aligned():
+    # every device buffer of the ABI is 16-byte aligned, the RoPE tables included
+    assert _code(msa.msa_rope_table, MIS, A, 16, 128, 1e4, 0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_rope_table, A, MIS, 16, 128, 1e4, 0) == L.MSA_ERR_ARG
+    lay = msa.msa_bank_layout([512] * 4, 128)
+    tok, ch = lay["doc_tok_off"], lay["doc_chunk_off"]
+    b = _bank(doc_tok_off_host=tok.ctypes.data, doc_chunk_off_host=ch.ctypes.data)
+    assert _code(msa.msa_pool_memory, b, A, A, A, 0, 1, _rope(max_pos=512, cos=MIS.addr), 0) == L.MSA_ERR_ARG
+    assert "rope.cos" in msa.msa_last_error()
