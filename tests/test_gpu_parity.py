@@ -109,6 +109,24 @@ def test_pool_edge_lengths(device, dtype):
     _check_pool(w, ob, bank)
 
 
+# bf16 head shapes: rows of whole 1 KB pieces (h_kv d and h_r d_r multiples of
+# 512: one wave per piece, 3 to 16 pieces) and rows that are not (the head-row
+# kernel), on ragged documents
+@pytest.mark.parametrize("h_kv,d,h_r,d_r", [(8, 64, 8, 64), (4, 128, 4, 256), (8, 128, 2, 256), (16, 128, 8, 128),
+                                             (8, 64, 4, 128), (4, 128, 8, 64), (2, 64, 2, 64), (4, 64, 2, 128)])
+def test_pool_head_shapes(device, h_kv, d, h_r, d_r):
+    base = _wl("prefill-16k")
+    C = base.chunk
+    lens = np.array([1, C - 1, C, C + 1, 2 * C + 5, 5, C // 2, 5 * C - 3], dtype=np.int64)
+    w = dataclasses.replace(base, doc_lens=lens, h_kv=h_kv, d=d, h_r=h_r, d_r=d_r, h_q=h_kv,
+                            gold=np.zeros((1, 0), np.int64))
+    log(f"pool shapes h_kv={h_kv} d={d} h_r={h_r} d_r={d_r}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    bank, _ = gpu_bank_pooled(w, K, V, KR, device, 2)
+    _check_pool(w, ob, bank)
+
+
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name,t_r,n_q", [("tiny", 16, 1), ("16k", 128, 1), ("16k", 1, 1), ("16k", 5, 3),
                                           ("16k", 40, 2), ("16k", 16, 3), ("16k", 1, 37), ("16k", 48, 3),
