@@ -581,7 +581,7 @@ def main() -> int:
 
     # the scan's access pattern without its arithmetic (read-only probe), same launches
     n_probe = max(10, args.steps // 2)
-    pws_n = (w.n_chunks + 15) // 16 * 128
+    pws_n = L.msa_route_workspace_bytes(bank.c, 1, 1)
     pws = M.workspace(pws_n, dev)
     for _ in range(3):
         L.msa_scan_read_probe(bank.c, pws, pws_n)

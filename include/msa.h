@@ -261,8 +261,8 @@ int msa_sparse_attend(const msa_bank *b, const void *Q, const void *K_loc, const
  * duration is the practical floor of msa_route_score's scan on this device
  * (the nominal HBM peak is not reachable by any access pattern); bench.py
  * reports the scan against both.  bf16 banks with h_r = 8, d_r = 128 only
- * (else MSA_ERR_UNSUPPORTED).  ws: at least ceil(n_chunks / 16) * 128 bytes,
- * 16-byte aligned, contents overwritten (MSA_ERR_WORKSPACE otherwise).
+ * (else MSA_ERR_UNSUPPORTED).  ws: at least msa_route_workspace_bytes(b, 1, 1)
+ * bytes, 16-byte aligned, contents overwritten (MSA_ERR_WORKSPACE otherwise).
  */
 int msa_scan_read_probe(const msa_bank *b, void *ws, size_t ws_bytes, void *stream);
 

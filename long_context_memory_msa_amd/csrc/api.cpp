@@ -144,7 +144,10 @@ msa::RouteArgs route_args(const msa_bank *b, const void *qr, int32_t n_q, int32_
                           float *doc_scores, uint32_t *doc_keys, uint32_t *chunk_out) {
   msa::RouteArgs a;
   a.doc_chunk_off = b->doc_chunk_off;
-  a.edges = edges;
+  a.edges = edges;  // single-writer workspace: the records, then the interior-document scores
+  a.dsc = edges && msa::route_single_writer(t_r)
+              ? edges + msa::route_record_bytes(b->n_chunks, n_q, t_r) / sizeof(float)
+              : nullptr;
   a.doc_scores = doc_scores;
   a.dtype = b->dtype;
   a.h_r = b->h_r;
@@ -177,7 +180,7 @@ struct LayerWs {
 LayerWs layer_ws(const msa_bank *b, int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k) {
   LayerWs w;
   w.scores = align_up((size_t)n_q * b->n_docs * sizeof(uint32_t));
-  w.route = align_up(msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, n_q, t_r));
+  w.route = align_up(msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, b->n_docs, n_q, t_r));
   w.topk = align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
   msa::AttendArgs a = attend_args(b, nullptr, nullptr, nullptr, n_q, T, L_loc, h_q, nullptr, k, 0, 1.f, nullptr, nullptr);
   w.attend = align_up(msa::attend_ws_bytes(a));
@@ -255,9 +258,9 @@ struct LayerCtx {
   float *scores(float *s_doc) const { return s_doc ? s_doc : reinterpret_cast<float *>(w); }
 };
 
-// First half: the router scan.  Single-writer scans store the scores of the
-// documents inside one tile and per-tile edge records; otherwise the
-// document keys are zeroed and maxed atomically.
+// First half: the router scan.  Single-writer scans leave per-tile edge
+// records and the scores of the documents inside one tile in the route
+// workspace; otherwise the document keys are zeroed and maxed atomically.
 hipError_t layer_route(const LayerCtx &c, const void *QR, float *s_doc) {
   hipError_t e = hipSuccess;
   if (msa::route_single_writer(c.t_r)) {
@@ -295,16 +298,15 @@ hipError_t layer_tail(const LayerCtx &c, const void *Q, const void *K_loc, const
     float *scores = c.scores(s_doc);
     msa::RouteArgs ra = route_args(b, nullptr, c.n_q, c.t_r, static_cast<float *>(c.rt_ws()), scores, nullptr,
                                    nullptr);
-    // documents on tile edges come from the scan's records: a single-pass
-    // top-k resolves them as it loads, the sliced one after a resolve kernel
-    // (coalesced over queries)
+    // the document scores come from the scan's records and interior scores:
+    // a single-pass top-k completes them as it loads, the sliced one after a
+    // resolve kernel (coalesced over queries)
     msa::TopkSrc src{};
     src.scores = scores;
     if (msa::topk_single_pass(b->n_docs)) {
       src.mode = msa::TopkSrc::EDGES;
-      src.edges = ra.edges;
+      src.edges = msa::edge_layout(ra);
       src.doc_chunk_off = b->doc_chunk_off;
-      src.n_tiles = (b->n_chunks + 15) / 16;
       src.t_r = c.t_r;
     } else {
       src.mode = msa::TopkSrc::SCORES;
@@ -484,7 +486,7 @@ int msa_pool_memory(const msa_bank *b, const void *K, const void *V, const void 
 
 size_t msa_route_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t t_r) {
   if (!b || n_q < 1 || t_r < 1 || b->n_chunks < 1) return 0;
-  return msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, n_q, t_r);
+  return msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, b->n_docs, n_q, t_r);
 }
 
 int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r, float *s_doc, float *s_chunk,
@@ -497,7 +499,7 @@ int msa_route_score(const msa_bank *b, const void *qr, int32_t n_q, int32_t t_r,
     if (max_wg_per_cu < 0) return fail(MSA_ERR_ARG, "max_wg_per_cu must be >= 0");
     CHECK_PTR(s_doc, 4, "s_doc");
     if (s_chunk && !aligned(s_chunk, 4)) return fail(MSA_ERR_ARG, "s_chunk is not 4-byte aligned");
-    const size_t need = msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, n_q, t_r);
+    const size_t need = msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, b->n_docs, n_q, t_r);
     if (need && (!ws || ws_bytes < need || !aligned(ws, 16)))
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
     hipStream_t s = (hipStream_t)stream;
@@ -532,7 +534,7 @@ int msa_scan_read_probe(const msa_bank *b, void *ws, size_t ws_bytes, void *stre
     if (rc) return rc;
     if (b->dtype != MSA_BF16 || b->h_r != 8 || b->d_r != 128)
       return fail(MSA_ERR_UNSUPPORTED, "the probe mirrors the bf16 scan with 8 router heads of 128");
-    const size_t need = (size_t)((b->n_chunks + 15) / 16) * 32 * sizeof(float);
+    const size_t need = msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, b->n_docs, 1, 1);
     if (!ws || ws_bytes < need || !aligned(ws, 16))
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need, ws_bytes);
     const msa::RouteArgs a = route_args(b, nullptr, 1, 1, static_cast<float *>(ws), nullptr, nullptr, nullptr);

@@ -42,8 +42,11 @@ struct RouteArgs {
   const int64_t *doc_chunk_off;  // device [n_docs+1]
   const void *qr;                // [n_q][t_r][h_r][d_r]
   int n_q, t_r;
-  // single-writer mode (edges != null): fp32 scores written directly
-  float *edges;                  // [row blocks][tiles][2][16] per-tile segment records
+  // single-writer mode (edges != null): per-tile records and the scores of the
+  // documents inside one tile (layout: EdgeLayout below); a resolve pass or a
+  // record-reading top-k writes doc_scores
+  float *edges;                  // records
+  float *dsc = nullptr;          // [row blocks][n_docs][16 or 1] scores of documents inside one tile
   float *doc_scores;             // [n_q][n_docs] fp32
   // atomic mode (edges == null): order-preserving keys, zeroed before the scan
   uint32_t *doc_keys;            // [n_q][n_docs]
@@ -62,7 +65,9 @@ struct RouteArgs {
 bool route_single_writer(int t_r);                    // (query, document) scores have one writer
 bool route_use_wide(int dtype, int h_r, int d_r, int t_r);     // GEMM-tiled scan for many rows per query
 size_t route_wide_ws_bytes(int n_q, int t_r, int h_r);
-size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_q, int t_r);
+size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_docs, int n_q, int t_r);
+// single-writer workspace: the records (this many bytes, a multiple of 256), then the interior-document scores
+size_t route_record_bytes(int64_t n_chunks, int n_q, int t_r);
 hipError_t launch_route_wide(const RouteArgs &a, hipStream_t s);
 hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s);
 // read-only probe of the decode scan's traffic (bf16, 8 x 128 router heads);
@@ -72,30 +77,37 @@ hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);
 hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s);  // in place
 
-// Score of document `doc` for query `q` in single-writer mode.  The scan stores
-// a document that lies strictly inside one 16-chunk tile itself; for the others
-// it writes per-tile records [row block][tile][first segment 0..15 | last
-// segment 16..31][row], and the document's score is the max of its last
-// segment in the first tile it touches and its first segments in the later ones.
-// Returns false for an interior document (its score is the stored one), else
-// true with the score from the records in *v.
-__device__ __forceinline__ bool edge_doc_score(const float *edges, const int64_t *doc_chunk_off, int64_t n_tiles,
-                                               int t_r, int q, int doc, float *v) {
+// Single-writer scan output (one writer per (query, document) score).  Per
+// 16-chunk tile a record rec[row block][tile][first segment 0..15 | last
+// segment 16..31] holds the maxima of the tile's first and last document
+// segments for the rows of the block (16 rows when t_r == 1, row 0 when
+// t_r == 16).  A document strictly inside one tile has its scores for the
+// block's rows in one row of the document-major array dsc[row block][doc][rw]
+// (one 64-byte store instead of a scattered store per query).
+struct EdgeLayout {
+  const float *rec = nullptr;
+  const float *dsc = nullptr;
+  int64_t n_tiles = 0;
+  int rw = 16;  // rows per document in dsc
+};
+EdgeLayout edge_layout(const RouteArgs &a);
+
+// Score of document `doc` for query `q` from a single-writer scan's output:
+// for a document inside one tile the stored score, otherwise the max of its
+// last segment in the first tile it touches and its first segments in the
+// later ones.
+__device__ __forceinline__ float edge_doc_score(const EdgeLayout &L, const int64_t *doc_chunk_off, int n_docs, int t_r,
+                                                int q, int doc) {
   const int rb = t_r == 1 ? q / 16 : q;  // row block of this query
-  const int r = t_r == 1 ? q % 16 : 0;   // its row within the block's records
+  const int r = t_r == 1 ? q % 16 : 0;   // its row within the block
   const int64_t c0 = doc_chunk_off[doc], c1 = doc_chunk_off[doc + 1] - 1;
   const int64_t ta = c0 / 16, tb = c1 / 16;
-  if (ta == tb && (c0 % 16) != 0 && (c1 % 16) != 15) return false;  // interior: stored by the scan
-  const float *rec = edges + (int64_t)rb * n_tiles * 32;
-  float m;
-  if (ta == tb) {
-    m = rec[ta * 32 + ((c0 % 16) == 0 ? 0 : 16) + r];
-  } else {
-    m = rec[ta * 32 + 16 + r];
-    for (int64_t t = ta + 1; t <= tb; ++t) m = fmaxf(m, rec[t * 32 + r]);
-  }
-  *v = m;
-  return true;
+  if (ta == tb && (c0 % 16) != 0 && (c1 % 16) != 15) return L.dsc[((int64_t)rb * n_docs + doc) * L.rw + r];
+  const float *rec = L.rec + (int64_t)rb * L.n_tiles * 32;
+  if (ta == tb) return rec[ta * 32 + ((c0 % 16) == 0 ? 0 : 16) + r];
+  float m = rec[ta * 32 + 16 + r];
+  for (int64_t t = ta + 1; t <= tb; ++t) m = fmaxf(m, rec[t * 32 + r]);
+  return m;
 }
 
 // ---- top-k -----------------------------------------------------------------
@@ -104,11 +116,10 @@ bool topk_single_pass(int n_docs);  // one workgroup per query, no workspace
 // Where the document scores [n_q][n_docs] come from
 struct TopkSrc {
   enum Mode { SCORES = 0, KEYS = 1, EDGES = 2 } mode;
-  float *scores;                 // SCORES: read; EDGES: interior documents read, the others written
+  float *scores;                 // SCORES: read; EDGES: written (the completed document scores)
   const uint32_t *keys;          // KEYS: order-preserving keys
-  const float *edges;            // EDGES: the scan's per-tile records
+  EdgeLayout edges;              // EDGES: the single-writer scan's output
   const int64_t *doc_chunk_off;  // EDGES
-  int64_t n_tiles;               // EDGES: 16-chunk tiles
   int t_r;                       // EDGES
 };
 hipError_t launch_topk(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,

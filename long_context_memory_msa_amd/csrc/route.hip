@@ -23,11 +23,14 @@
 //  * when every (query, document) score has a single writer (one query per
 //    row, or one row block per query) a tile emits one coalesced 128-byte
 //    record with the max of its first and of its last document segment per
-//    query, documents lying strictly inside the tile are stored directly, and
-//    a small second kernel resolves each document from the records of the
-//    tiles it spans -- no atomics and no zero fill; otherwise each segment
-//    goes out as an order-preserving atomicMax on uint32 keys.
+//    query; a document lying strictly inside the tile has its scores for the
+//    block's rows stored as one 64-byte row of a document-major array (16
+//    scattered 4-byte stores per document into [query][document] scores had
+//    cost the scan 2-3 %); a small second kernel then writes every document
+//    score from these -- no atomics and no zero fill.  Otherwise each
+//    segment goes out as an order-preserving atomicMax on uint32 keys.
 #include <algorithm>
+#include <atomic>
 
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
@@ -290,14 +293,15 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
       }
       v = seg_scan16(cv ? v : -INFINITY, match);
       if constexpr (EDGE) {
+        // (single writer with t_r % 16 == 0: the row block is query q, one row per document)
         const float first = __shfl(v, tail0, 16), last = __shfl(v, 15, 16);
-        if (G == 0 && tail && doc >= 0 && doc != d0 && doc != d15) a.doc_scores[(int64_t)q * a.n_docs + doc] = v;
+        if (G == 0 && tail && doc >= 0 && doc != d0 && doc != d15) a.dsc[(int64_t)rb * a.n_docs + doc] = v;
         if (G == 0 && col < 2) erec[col * 16] = col == 0 ? first : last;
       } else {
         if (G == 0 && tail && doc >= 0) atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(v));
       }
     } else {
-      float first[4], last[4];
+      float first[4], last[4], sv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = rowq[i];
@@ -310,13 +314,17 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
         if constexpr (EDGE) {
           first[i] = __shfl(v, tail0, 16);
           last[i] = __shfl(v, 15, 16);
-          if (tail && doc >= 0 && doc != d0 && doc != d15 && q >= 0) a.doc_scores[(int64_t)q * a.n_docs + doc] = v;
+          sv[i] = v;
         } else {
           if (tail && doc >= 0 && q >= 0) atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(v));
         }
       }
       if constexpr (EDGE) {
-        // one 128-byte record per tile: lanes (G, col 0) write the first-segment maxima
+        // a document strictly inside the tile: its 16 rows as one 64-byte row
+        // (rows past n_rows hold unused values)
+        if (tail && doc >= 0 && doc != d0 && doc != d15)
+          reinterpret_cast<float4 *>(a.dsc + ((int64_t)rb * a.n_docs + doc) * 16)[G] = float4{sv[0], sv[1], sv[2], sv[3]};
+        // one 128-byte record per tile: lanes (G, col 0) hold the first-segment maxima
         // of rows 4G..4G+3, lanes (G, col 1) the last-segment maxima
         if (col < 2) {
           const float *src = col == 0 ? first : last;
@@ -327,19 +335,17 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
   }
 }
 
-// Document scores from the per-tile records (single-writer mode): a document
-// spanning tiles ta..tb is the last segment of ta and the first segment of
-// every later tile it reaches; a document strictly inside one tile was
-// stored by the scan itself.
-__global__ void resolve_docs_kernel(const float *edges, const int64_t *doc_chunk_off, int n_q, int n_docs,
-                                    int64_t n_tiles, int t_r, float *doc_scores) {
-  // query fastest: the lanes of a wave read consecutive rows of the same tile records
+// Every document score (single-writer mode): a document spanning tiles
+// ta..tb is the max of the last segment of ta and the first segment of every
+// later tile it reaches (per-tile records); a document strictly inside one
+// tile is copied from the scan's document-major scores.
+__global__ void resolve_docs_kernel(EdgeLayout L, const int64_t *doc_chunk_off, int n_q, int n_docs, int t_r,
+                                    float *doc_scores) {
+  // query fastest: the lanes of a wave read consecutive rows of the same records
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)n_q * n_docs) return;
   const int q = (int)(i % n_q), doc = (int)(i / n_q);
-  float *out = doc_scores + (int64_t)q * n_docs + doc;
-  float v;
-  if (edge_doc_score(edges, doc_chunk_off, n_tiles, t_r, q, doc, &v)) *out = v;
+  doc_scores[(int64_t)q * n_docs + doc] = edge_doc_score(L, doc_chunk_off, n_docs, t_r, q, doc);
 }
 
 // Bandwidth probe: the decode scan's memory traffic without its arithmetic.
@@ -374,39 +380,57 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void scan_read_probe_kernel(R
   }
 }
 
+struct ScanGrid {
+  int64_t wgs = 1, n_waves = 4;
+};
+
+// Persistent grid of the streaming scan: as many workgroups as stay resident
+// together (occupancy of this kernel x compute units, at most max_wg_per_cu
+// per CU when the caller caps it), so no second, partial round.
 template <typename T, int HR, int DR, bool EDGE>
-hipError_t route_launch(const RouteArgs &a, hipStream_t s) {
-  // Persistent grid: exactly as many workgroups as stay resident together
-  // (occupancy of this kernel x compute units), so no second, partial round.
-  static int resident = 0;  // workgroups per CU for this instantiation
-  if (resident == 0) {
+ScanGrid grid_of(const RouteArgs &a) {
+  static std::atomic<int> resident{0};  // workgroups per CU for this instantiation
+  int res = resident.load(std::memory_order_relaxed);
+  if (res == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, route_scan_kernel<T, HR, DR, EDGE>, 256, 0) != hipSuccess ||
         n < 1)
       n = 1;
-    resident = MSA_ROUTE_WGCU > 0 && MSA_ROUTE_WGCU < n ? MSA_ROUTE_WGCU : n;
+    res = MSA_ROUTE_WGCU > 0 && MSA_ROUTE_WGCU < n ? MSA_ROUTE_WGCU : n;
+    resident.store(res, std::memory_order_relaxed);
   }
-  const int64_t n_tiles = (a.n_chunks + 15) / 16;
-  const int n_rows = a.n_q * a.t_r;
-  const int rbs = (n_rows + 15) / 16;
   // a caller that runs other kernels beside the scan (a pipelined decode step)
   // caps the workgroups per compute unit: while every compute unit holds more
   // than one of the scan's persistent workgroups, kernels on other streams
   // wait for the scan's waves to retire
-  const int per_cu = a.max_wg_per_cu > 0 && a.max_wg_per_cu < resident ? a.max_wg_per_cu : resident;
+  const int per_cu = a.max_wg_per_cu > 0 && a.max_wg_per_cu < res ? a.max_wg_per_cu : res;
+  const int64_t n_tiles = (a.n_chunks + 15) / 16;
+  const int rbs = (a.n_q * a.t_r + 15) / 16;
   const int64_t slots = (int64_t)device_cu_count() * per_cu;  // resident workgroups
   int64_t wgs = std::max<int64_t>(1, slots / rbs);
-  wgs = std::min<int64_t>(wgs, (n_tiles + 3) / 4);
+  wgs = std::max<int64_t>(1, std::min<int64_t>(wgs, (n_tiles + 3) / 4));
 #if MSA_ROUTE_BALANCE
   // Balance: as few waves as still need the same number of rounds, so that
   // (nearly) every wave streams the same number of tiles and no small set of
   // waves finishes a last, partial round alone at a fraction of the bandwidth.
-  const int64_t rounds = (n_tiles + 4 * wgs - 1) / (4 * wgs);
-  wgs = (n_tiles + 4 * rounds - 1) / (4 * rounds);
+  if (n_tiles > 0) {
+    const int64_t rounds = (n_tiles + 4 * wgs - 1) / (4 * wgs);
+    wgs = (n_tiles + 4 * rounds - 1) / (4 * rounds);
+  }
 #endif
-  const int64_t n_waves = wgs * 4;  // wave w starts at tile w
-  dim3 grid((unsigned)wgs, (unsigned)rbs), block(256);
-  hipLaunchKernelGGL((route_scan_kernel<T, HR, DR, EDGE>), grid, block, 0, s, a, n_tiles, n_waves);
+  ScanGrid g;
+  g.wgs = wgs;
+  g.n_waves = wgs * 4;  // wave w starts at tile w
+  return g;
+}
+
+template <typename T, int HR, int DR, bool EDGE>
+hipError_t route_launch(const RouteArgs &a, hipStream_t s) {
+  const ScanGrid g = grid_of<T, HR, DR, EDGE>(a);
+  const int64_t n_tiles = (a.n_chunks + 15) / 16;
+  const int rbs = (a.n_q * a.t_r + 15) / 16;
+  dim3 grid((unsigned)g.wgs, (unsigned)rbs), block(256);
+  hipLaunchKernelGGL((route_scan_kernel<T, HR, DR, EDGE>), grid, block, 0, s, a, n_tiles, g.n_waves);
   return hipGetLastError();
 }
 
@@ -433,6 +457,15 @@ hipError_t route_by_hr(const RouteArgs &a, hipStream_t s) {
 
 }  // namespace
 
+EdgeLayout edge_layout(const RouteArgs &a) {
+  EdgeLayout L;
+  L.rec = a.edges;
+  L.dsc = a.dsc;
+  L.n_tiles = (a.n_chunks + 15) / 16;
+  L.rw = a.t_r == 1 ? 16 : 1;
+  return L;
+}
+
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s) {
   if (n == 0) return hipSuccess;
   size_t g = std::min<size_t>((n + 255) / 256, 8192);
@@ -452,23 +485,27 @@ bool route_single_writer(int t_r) { return t_r == 1 || t_r == 16; }
 hipError_t launch_scan_read_probe(const RouteArgs &a, hipStream_t s) {
   if (a.n_chunks == 0) return hipSuccess;
   if (a.dtype != 1 || a.h_r != 8 || a.d_r != 128) return hipErrorInvalidValue;
-  // the decode scan's grid (one row block): resident workgroups, balanced
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, route_scan_kernel<bf16_t, 8, 128, true>, 256, 0) != hipSuccess ||
-      n < 1)
-    n = 1;
+  // the decode scan's grid (one row block, full occupancy)
+  RouteArgs d = a;
+  d.n_q = 1;
+  d.t_r = 1;
+  d.max_wg_per_cu = 0;
+  const ScanGrid g = grid_of<bf16_t, 8, 128, true>(d);
   const int64_t n_tiles = (a.n_chunks + 15) / 16;
-  int64_t wgs = std::min<int64_t>((int64_t)device_cu_count() * n, (n_tiles + 3) / 4);
-  const int64_t rounds = (n_tiles + 4 * wgs - 1) / (4 * wgs);
-  wgs = (n_tiles + 4 * rounds - 1) / (4 * rounds);
-  hipLaunchKernelGGL((scan_read_probe_kernel<8, 128>), dim3((unsigned)wgs), dim3(256), 0, s, a, n_tiles, wgs * 4);
+  hipLaunchKernelGGL((scan_read_probe_kernel<8, 128>), dim3((unsigned)g.wgs), dim3(256), 0, s, a, n_tiles, g.n_waves);
   return hipGetLastError();
 }
 
-size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_q, int t_r) {
+size_t route_record_bytes(int64_t n_chunks, int n_q, int t_r) {
+  const int64_t rbs = ((int64_t)n_q * t_r + 15) / 16;
+  return ((size_t)rbs * ((n_chunks + 15) / 16) * 32 * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_docs, int n_q, int t_r) {
   if (route_single_writer(t_r)) {
+    // records, then the scores of the documents inside one tile [row block][doc][16 or 1]
     const int64_t rbs = ((int64_t)n_q * t_r + 15) / 16;
-    return (size_t)rbs * ((n_chunks + 15) / 16) * 32 * sizeof(float);
+    return route_record_bytes(n_chunks, n_q, t_r) + (size_t)rbs * n_docs * (t_r == 1 ? 16 : 1) * sizeof(float);
   }
   if (route_use_wide(dtype, h_r, d_r, t_r)) return route_wide_ws_bytes(n_q, t_r, h_r);
   return 0;
@@ -476,8 +513,8 @@ size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_q, in
 
 hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s) {
   const int64_t n = (int64_t)a.n_q * a.n_docs;
-  hipLaunchKernelGGL(resolve_docs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.edges,
-                     a.doc_chunk_off, a.n_q, a.n_docs, (a.n_chunks + 15) / 16, a.t_r, a.doc_scores);
+  hipLaunchKernelGGL(resolve_docs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, edge_layout(a),
+                     a.doc_chunk_off, a.n_q, a.n_docs, a.t_r, a.doc_scores);
   return hipGetLastError();
 }
 

@@ -199,11 +199,8 @@ __device__ __forceinline__ uint64_t load_composite(const TopkSrc &src, int q, in
   } else if constexpr (MODE == TopkSrc::SCORES) {
     key = score_key(src.scores[at]);
   } else {
-    float v;
-    if (edge_doc_score(src.edges, src.doc_chunk_off, src.n_tiles, src.t_r, q, doc, &v))
-      src.scores[at] = v;  // complete the document scores for the caller
-    else
-      v = src.scores[at];
+    const float v = edge_doc_score(src.edges, src.doc_chunk_off, n_docs, src.t_r, q, doc);
+    src.scores[at] = v;  // complete the document scores for the caller
     key = score_key(v);
   }
   return composite(key, doc);

@@ -234,7 +234,7 @@ def test_layer_halves_validation():
 
 def test_scan_read_probe_validation():
     b = _bank()
-    need = (b.n_chunks + 15) // 16 * 128
+    need = msa.msa_route_workspace_bytes(b, 1, 1)
     assert _code(msa.msa_scan_read_probe, b, A, need - 1, stream=0) == L.MSA_ERR_WORKSPACE
     assert _code(msa.msa_scan_read_probe, b, None, need, stream=0) == L.MSA_ERR_WORKSPACE
     assert _code(msa.msa_scan_read_probe, _bank(dtype=L.MSA_F32), A, need, stream=0) == L.MSA_ERR_UNSUPPORTED

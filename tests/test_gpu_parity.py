@@ -491,15 +491,17 @@ def test_layer_degenerate_banks(device, lens, k, t_r):
 
 def test_scan_read_probe_runs(device):
     # the bandwidth probe reads the bank in the scan's pattern and writes one
-    # finite record per 16-chunk tile (its values carry no meaning)
+    # finite record per 16-chunk tile (its values carry no meaning) into the
+    # slots of the scan's record layout
     w = _wl("decode-100m", 700_000)
     qi, K, V, KR = host_inputs(w)
     bank, _ = gpu_bank_pooled(w, K, V, KR, device, 1)
     n_tiles = (w.n_chunks + 15) // 16
-    ws = torch.full((n_tiles * 32,), float("nan"), dtype=torch.float32, device=device)
-    L.msa_scan_read_probe(bank.c, ws, ws.numel() * 4)
+    nb = L.msa_route_workspace_bytes(bank.c, 1, 1)
+    ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=device)
+    L.msa_scan_read_probe(bank.c, ws, nb)
     torch.cuda.synchronize()
-    assert torch.isfinite(ws).all()
+    assert int(torch.isfinite(ws).sum()) >= n_tiles * 32
 
 
 def test_interleave_small(device):
