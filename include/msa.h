@@ -257,7 +257,7 @@ int msa_sparse_attend(const msa_bank *b, const void *Q, const void *K_loc, const
  * Measurement aid (no part of the method): reads the bank's router keys,
  * inverse norms and chunk->document ids with exactly the access pattern,
  * grid and tile order of the decode router scan (t_r = 1), without its
- * arithmetic, and writes one 128-byte record per 16-chunk tile into ws.  Its
+ * arithmetic, and writes one 128-byte record per pair of 16-chunk tiles into ws.  Its
  * duration is the practical floor of msa_route_score's scan on this device
  * (the nominal HBM peak is not reachable by any access pattern); bench.py
  * reports the scan against both.  bf16 banks with h_r = 8, d_r = 128 only

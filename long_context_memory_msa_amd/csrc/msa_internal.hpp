@@ -77,34 +77,35 @@ hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);
 hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s);  // in place
 
-// Single-writer scan output (one writer per (query, document) score).  Per
-// 16-chunk tile a record rec[row block][tile][first segment 0..15 | last
-// segment 16..31] holds the maxima of the tile's first and last document
-// segments for the rows of the block (16 rows when t_r == 1, row 0 when
-// t_r == 16).  A document strictly inside one tile has its scores for the
-// block's rows in one row of the document-major array dsc[row block][doc][rw]
-// (one 64-byte store instead of a scattered store per query).
+// Single-writer scan output (one writer per (query, document) score).  The
+// scan takes its 16-chunk tiles in pairs, so its unit is 32 chunks: per unit
+// a record rec[row block][unit][first segment 0..15 | last segment 16..31]
+// holds the maxima of the unit's first and last document segments for the
+// rows of the block (16 rows when t_r == 1, row 0 when t_r == 16).  A
+// document strictly inside one unit has its scores for the block's rows in
+// one row of the document-major array dsc[row block][doc][rw] (one 64-byte
+// store instead of a scattered store per query).
 struct EdgeLayout {
   const float *rec = nullptr;
   const float *dsc = nullptr;
-  int64_t n_tiles = 0;
+  int64_t n_units = 0;
   int rw = 16;  // rows per document in dsc
 };
 EdgeLayout edge_layout(const RouteArgs &a);
 
 // Score of document `doc` for query `q` from a single-writer scan's output:
-// for a document inside one tile the stored score, otherwise the max of its
-// last segment in the first tile it touches and its first segments in the
+// for a document inside one unit the stored score, otherwise the max of its
+// last segment in the first unit it touches and its first segments in the
 // later ones.
 __device__ __forceinline__ float edge_doc_score(const EdgeLayout &L, const int64_t *doc_chunk_off, int n_docs, int t_r,
                                                 int q, int doc) {
   const int rb = t_r == 1 ? q / 16 : q;  // row block of this query
   const int r = t_r == 1 ? q % 16 : 0;   // its row within the block
   const int64_t c0 = doc_chunk_off[doc], c1 = doc_chunk_off[doc + 1] - 1;
-  const int64_t ta = c0 / 16, tb = c1 / 16;
-  if (ta == tb && (c0 % 16) != 0 && (c1 % 16) != 15) return L.dsc[((int64_t)rb * n_docs + doc) * L.rw + r];
-  const float *rec = L.rec + (int64_t)rb * L.n_tiles * 32;
-  if (ta == tb) return rec[ta * 32 + ((c0 % 16) == 0 ? 0 : 16) + r];
+  const int64_t ta = c0 / 32, tb = c1 / 32;
+  if (ta == tb && (c0 % 32) != 0 && (c1 % 32) != 31) return L.dsc[((int64_t)rb * n_docs + doc) * L.rw + r];
+  const float *rec = L.rec + (int64_t)rb * L.n_units * 32;
+  if (ta == tb) return rec[ta * 32 + ((c0 % 32) == 0 ? 0 : 16) + r];
   float m = rec[ta * 32 + 16 + r];
   for (int64_t t = ta + 1; t <= tb; ++t) m = fmaxf(m, rec[t * 32 + r]);
   return m;

@@ -21,14 +21,18 @@
 //  * persistent waves take tiles in an interleaved order (wave w: tiles w,
 //    w + W, ...), so the waves stream one compact window of the bank;
 //  * when every (query, document) score has a single writer (one query per
-//    row, or one row block per query) a tile emits one coalesced 128-byte
-//    record with the max of its first and of its last document segment per
-//    query; a document lying strictly inside the tile has its scores for the
-//    block's rows stored as one 64-byte row of a document-major array (16
-//    scattered 4-byte stores per document into [query][document] scores had
-//    cost the scan 2-3 %); a small second kernel then writes every document
-//    score from these -- no atomics and no zero fill.  Otherwise each
-//    segment goes out as an order-preserving atomicMax on uint32 keys.
+//    row, or one row block per query) the waves take their tiles in pairs of
+//    consecutive tiles, carry the document open at the end of the first
+//    tile into the second, and emit one coalesced 128-byte record per pair
+//    with the max of its first and of its last document segment per query; a
+//    document lying strictly inside the pair has its scores for the block's
+//    rows stored as one 64-byte row of a document-major array; a small
+//    second kernel then writes every document score from these -- no
+//    atomics and no zero fill.  Stores inside the 1.65 GB read stream are
+//    costly: 16 scattered 4-byte stores per interior document had cost the
+//    scan 2-3 %, a record per tile instead of per pair another 3 %.
+//    Otherwise each segment goes out as an order-preserving atomicMax on
+//    uint32 keys.
 #include <algorithm>
 #include <atomic>
 
@@ -123,7 +127,9 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
   }
   // interleaved tile order: at any moment the waves stream one compact window
   const int64_t wave_id = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t t_lo = wave_id, t_hi = n_tiles, t_step = n_waves;
+  // wave w takes the pairs of consecutive tiles w, w + W, ... (tiles 2p, 2p + 1)
+  auto tile_of = [&](int64_t j) { return 2 * (wave_id + (j >> 1) * n_waves) + (j & 1); };
+  const int64_t t_lo = tile_of(0), t_hi = n_tiles;
   const T *krbar = static_cast<const T *>(a.krbar);
 
   // Prefetch ring: the key fragments of PD (tile, head) steps are in flight
@@ -216,8 +222,17 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
 #define MSA_QOP(f) qfrag[(f) + zoff][lane]
 #endif
 
-  for (int64_t tile = t_lo; tile < t_hi; tile += t_step) {
-    const int64_t tile_next = tile + t_step;
+  // single writer: a record per pair of tiles (a 32-chunk unit); the open
+  // document of the pair's first tile is carried into its second
+  float carry[4] = {0.f, 0.f, 0.f, 0.f};  // running max of that document (per row)
+  float rfirst[4] = {0.f, 0.f, 0.f, 0.f};  // the pair's first-segment maxima, once closed
+  int cdoc = -2;                          // the carried document (-2: none)
+  bool first_open = false;                // the pair's first document runs on into the second tile
+  for (int64_t j = 0;; ++j) {
+    const int64_t tile = tile_of(j);
+    if (tile >= t_hi) break;
+    const int kk = (int)(j & 1);  // first / second tile of the pair
+    const int64_t tile_next = tile_of(j + 1);
     const int64_t c = tile * 16 + col;
     const bool cv = c < a.n_chunks;
     // The loads for the next tile are issued unconditionally (after the
@@ -280,7 +295,13 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
     // last column holding the tile's first document (documents are contiguous)
     const unsigned long long same0 = __ballot(doc == d0);
     const int tail0 = __popcll((same0 >> (16 * G)) & 0xFFFFull) - 1;
-    float *erec = EDGE ? a.edges + (rb * n_tiles + tile) * 32 : nullptr;  // [2][16] floats
+    // the pair's tiles: a second tile follows this one in the same pair
+    const bool pair2 = kk == 0 && has_next;
+    const int dn0 = __shfl(doc_cur, 0, 16);  // (doc_cur now holds the next tile's documents)
+    const bool cont = pair2 && d15 >= 0 && dn0 == d15;  // this tile's last document runs on into the next
+    const int64_t n_units = (n_tiles + 1) / 2;
+    float *erec = EDGE ? a.edges + (rb * n_units + (tile >> 1)) * 32 : nullptr;  // [2][16] floats
+    const bool rec_now = kk == 1 || !pair2;  // the pair ends with this tile
     if (uniform) {
       // every row of the block belongs to one query: max over the 16 rows first
       float v = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
@@ -294,14 +315,29 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
       v = seg_scan16(cv ? v : -INFINITY, match);
       if constexpr (EDGE) {
         // (single writer with t_r % 16 == 0: the row block is query q, one row per document)
-        const float first = __shfl(v, tail0, 16), last = __shfl(v, 15, 16);
-        if (G == 0 && tail && doc >= 0 && doc != d0 && doc != d15) a.dsc[(int64_t)rb * a.n_docs + doc] = v;
-        if (G == 0 && col < 2) erec[col * 16] = col == 0 ? first : last;
+        if (kk == 1 && doc == cdoc) v = fmaxf(v, carry[0]);
+        const float at_tail0 = __shfl(v, tail0, 16), at15 = __shfl(v, 15, 16);
+        const int dfirst_open = kk == 1 && first_open ? cdoc : -2;
+        const bool pair_first = kk == 0 ? doc == d0 : doc == dfirst_open;
+        const bool pair_last = rec_now && doc == d15;
+        const bool carried = kk == 0 && cont && doc == d15;
+        if (G == 0 && tail && doc >= 0 && !pair_first && !pair_last && !carried)
+          a.dsc[(int64_t)rb * a.n_docs + doc] = v;
+        if (kk == 0) {
+          first_open = cont && d0 == d15;
+          rfirst[0] = at_tail0;
+          carry[0] = at15;
+          cdoc = cont ? d15 : -2;
+        }
+        if (rec_now) {
+          const float first = (kk == 1 && first_open) ? at_tail0 : rfirst[0];
+          if (G == 0 && col < 2) erec[col * 16] = col == 0 ? first : at15;
+        }
       } else {
         if (G == 0 && tail && doc >= 0) atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(v));
       }
     } else {
-      float first[4], last[4], sv[4];
+      float at_tail0[4], at15[4], sv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = rowq[i];
@@ -312,22 +348,39 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
         }
         v = seg_scan16(cv ? v : -INFINITY, match);
         if constexpr (EDGE) {
-          first[i] = __shfl(v, tail0, 16);
-          last[i] = __shfl(v, 15, 16);
+          if (kk == 1 && doc == cdoc) v = fmaxf(v, carry[i]);
+          at_tail0[i] = __shfl(v, tail0, 16);
+          at15[i] = __shfl(v, 15, 16);
           sv[i] = v;
         } else {
           if (tail && doc >= 0 && q >= 0) atomicMax(a.doc_keys + (int64_t)q * a.n_docs + doc, score_key(v));
         }
       }
       if constexpr (EDGE) {
-        // a document strictly inside the tile: its 16 rows as one 64-byte row
+        // a document strictly inside the pair: its 16 rows as one 64-byte row
         // (rows past n_rows hold unused values)
-        if (tail && doc >= 0 && doc != d0 && doc != d15)
+        const int dfirst_open = kk == 1 && first_open ? cdoc : -2;
+        const bool pair_first = kk == 0 ? doc == d0 : doc == dfirst_open;
+        const bool pair_last = rec_now && doc == d15;
+        const bool carried = kk == 0 && cont && doc == d15;
+        if (tail && doc >= 0 && !pair_first && !pair_last && !carried)
           reinterpret_cast<float4 *>(a.dsc + ((int64_t)rb * a.n_docs + doc) * 16)[G] = float4{sv[0], sv[1], sv[2], sv[3]};
-        // one 128-byte record per tile: lanes (G, col 0) hold the first-segment maxima
+        float first[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) first[i] = (kk == 1 && first_open) ? at_tail0[i] : rfirst[i];
+        if (kk == 0) {
+          first_open = cont && d0 == d15;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            rfirst[i] = at_tail0[i];
+            carry[i] = at15[i];
+          }
+          cdoc = cont ? d15 : -2;
+        }
+        // one 128-byte record per pair: lanes (G, col 0) hold the first-segment maxima
         // of rows 4G..4G+3, lanes (G, col 1) the last-segment maxima
-        if (col < 2) {
-          const float *src = col == 0 ? first : last;
+        if (rec_now && col < 2) {
+          const float *src = col == 0 ? (kk == 0 ? at_tail0 : first) : at15;
           *reinterpret_cast<float4 *>(erec + col * 16 + 4 * G) = float4{src[0], src[1], src[2], src[3]};
         }
       }
@@ -335,10 +388,10 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
   }
 }
 
-// Every document score (single-writer mode): a document spanning tiles
-// ta..tb is the max of the last segment of ta and the first segment of every
-// later tile it reaches (per-tile records); a document strictly inside one
-// tile is copied from the scan's document-major scores.
+// Every document score (single-writer mode): a document spanning 32-chunk
+// units ua..ub is the max of the last segment of ua and the first segment of
+// every later unit it reaches (the records); a document strictly inside one
+// unit is copied from the scan's document-major scores.
 __global__ void resolve_docs_kernel(EdgeLayout L, const int64_t *doc_chunk_off, int n_q, int n_docs, int t_r,
                                     float *doc_scores) {
   // query fastest: the lanes of a wave read consecutive rows of the same records
@@ -349,10 +402,11 @@ __global__ void resolve_docs_kernel(EdgeLayout L, const int64_t *doc_chunk_off, 
 }
 
 // Bandwidth probe: the decode scan's memory traffic without its arithmetic.
-// Same persistent grid and tile order, the same 16-byte loads of each tile's
-// key rows (8 in flight per wave), the same inverse-norm and document-id
-// loads and one 128-byte record written per tile; the loaded words are only
-// XOR-folded.  Its time is the practical floor of the scan on this device.
+// Same persistent grid and tile order (pairs of tiles), the same 16-byte
+// loads of each tile's key rows (8 in flight per wave), the same inverse-norm
+// and document-id loads and one 128-byte record written per pair; the loaded
+// words are only XOR-folded.  Its time is the practical floor of the scan on
+// this device.
 template <int HR, int DR>
 __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void scan_read_probe_kernel(RouteArgs a, int64_t n_tiles,
                                                                                  int64_t n_waves) {
@@ -361,7 +415,10 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void scan_read_probe_kernel(R
   const int col = lane & 15, G = lane >> 4;
   const bf16_t *krbar = static_cast<const bf16_t *>(a.krbar);
   uint32_t acc = 0;
-  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < n_tiles; tile += n_waves) {
+  for (int64_t pr = (int64_t)blockIdx.x * 4 + wave; 2 * pr < n_tiles; pr += n_waves) {
+   for (int kk = 0; kk < 2; ++kk) {
+    const int64_t tile = 2 * pr + kk;
+    if (tile >= n_tiles) break;
     int64_t cp = tile * 16 + col;
     cp = cp < a.n_chunks ? cp : a.n_chunks - 1;
     const uint4 *row = reinterpret_cast<const uint4 *>(krbar + cp * (HR * DR)) + G;
@@ -376,7 +433,8 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void scan_read_probe_kernel(R
       acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     acc ^= __float_as_uint(m) ^ (uint32_t)d;
-    if (lane < 32) a.edges[tile * 32 + lane] = __uint_as_float(acc & 0x3FFFFFFFu);
+   }
+    if (lane < 32) a.edges[pr * 32 + lane] = __uint_as_float(acc & 0x3FFFFFFFu);
   }
 }
 
@@ -410,9 +468,12 @@ ScanGrid grid_of(const RouteArgs &a) {
   int64_t wgs = std::max<int64_t>(1, slots / rbs);
   wgs = std::max<int64_t>(1, std::min<int64_t>(wgs, (n_tiles + 3) / 4));
 #if MSA_ROUTE_BALANCE
-  // Balance: as few waves as still need the same number of rounds, so that
-  // (nearly) every wave streams the same number of tiles and no small set of
-  // waves finishes a last, partial round alone at a fraction of the bandwidth.
+  // Balance: as few waves as still need the same number of rounds of tiles,
+  // so that no small set of waves finishes a last, partial round alone at a
+  // fraction of the bandwidth.  (Counted in tiles although the waves take
+  // pairs of tiles: at the 100M-token decode workload this grid -- 729
+  // workgroups, 8 or 9 pairs per wave -- streams at 277 us, the one balanced
+  // in pairs -- 689 workgroups, 9 pairs each -- at 294 us, the full 768 at 291 us.)
   if (n_tiles > 0) {
     const int64_t rounds = (n_tiles + 4 * wgs - 1) / (4 * wgs);
     wgs = (n_tiles + 4 * rounds - 1) / (4 * rounds);
@@ -461,7 +522,7 @@ EdgeLayout edge_layout(const RouteArgs &a) {
   EdgeLayout L;
   L.rec = a.edges;
   L.dsc = a.dsc;
-  L.n_tiles = (a.n_chunks + 15) / 16;
+  L.n_units = (a.n_chunks + 31) / 32;
   L.rw = a.t_r == 1 ? 16 : 1;
   return L;
 }
@@ -498,7 +559,7 @@ hipError_t launch_scan_read_probe(const RouteArgs &a, hipStream_t s) {
 
 size_t route_record_bytes(int64_t n_chunks, int n_q, int t_r) {
   const int64_t rbs = ((int64_t)n_q * t_r + 15) / 16;
-  return ((size_t)rbs * ((n_chunks + 15) / 16) * 32 * sizeof(float) + 255) & ~(size_t)255;
+  return ((size_t)rbs * ((n_chunks + 31) / 32) * 32 * sizeof(float) + 255) & ~(size_t)255;
 }
 
 size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_docs, int n_q, int t_r) {
