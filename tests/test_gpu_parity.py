@@ -489,6 +489,44 @@ def test_layer_degenerate_banks(device, lens, k, t_r):
     assert_attention_close(host(out), o_ref)
 
 
+# the decode scan's 32-chunk units (pairs of tiles, the document open at the
+# end of the first tile carried into the second): documents of exactly one
+# tile or one pair, documents ending one chunk before or after a tile or pair
+# edge, one-chunk documents, a document crossing from one pair into the next,
+# odd tile counts (a last pair of one tile) and a last tile of one chunk; one
+# and two row blocks of single-token queries (t_r = 1) and one query per row
+# block (t_r = 16)
+@pytest.mark.parametrize("chunks", [
+    [16] * 7, [32] * 3 + [1], [15, 17, 1, 31, 33, 16, 2], [1] * 47, [5, 100, 3, 1], [16, 32, 16], [33],
+    [17, 15], [31, 1, 32, 30, 2, 1]])
+@pytest.mark.parametrize("t_r,n_q", [(1, 16), (1, 20), (16, 2)])
+def test_route_pair_units(device, chunks, t_r, n_q):
+    base = _wl("prefill-16k")
+    lens = np.asarray(chunks, dtype=np.int64) * base.chunk
+    lens[-1] -= 5  # a partial last chunk
+    w = dataclasses.replace(base, doc_lens=lens, n_q=n_q, gold=np.zeros((n_q, 0), np.int64))
+    log(f"route pair units chunks={chunks} t_r={t_r} n_q={n_q}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    QRh = qi["QR"][:, :t_r]
+    S = O.chunk_scores(QRh, ob["krbar"])
+    sd = O.doc_scores(S, ob["doc_chunk_off"])
+    bank, _ = gpu_bank_from_oracle(w, ob, device)
+    s_doc = torch.full((n_q, w.n_docs), float("nan"), dtype=torch.float32, device=device)
+    s_chunk = torch.empty((n_q, w.n_chunks), dtype=torch.float32, device=device)
+    nb = L.msa_route_workspace_bytes(bank.c, n_q, t_r)
+    ws = M.workspace(nb, device)
+    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc, s_chunk, ws, nb)
+    torch.cuda.synchronize()
+    assert np.abs(host(s_chunk) - S).max() <= 2e-3
+    assert np.abs(host(s_doc) - sd).max() <= 2e-3
+    # and through the pipeline's capped grid
+    s_doc2 = torch.full_like(s_doc, float("nan"))
+    L.msa_route_score(bank.c, dev(QRh, w.dtype, device), n_q, t_r, s_doc2, None, ws, nb, max_wg_per_cu=1)
+    torch.cuda.synchronize()
+    assert torch.equal(s_doc, s_doc2)
+
+
 def test_scan_read_probe_runs(device):
     # the bandwidth probe reads the bank in the scan's pattern and writes one
     # finite record per pair of 16-chunk tiles (its values carry no meaning),
