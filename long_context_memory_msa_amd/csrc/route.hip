@@ -301,7 +301,9 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
     const bool cont = pair2 && d15 >= 0 && dn0 == d15;  // this tile's last document runs on into the next
     const int64_t n_units = (n_tiles + 1) / 2;
     float *erec = EDGE ? a.edges + (rb * n_units + (tile >> 1)) * 32 : nullptr;  // [2][16] floats
-    const bool rec_now = kk == 1 || !pair2;  // the pair ends with this tile
+    // the pair ends with this tile; a pair of one tile (the bank's last tile
+    // alone) holds no chunk 31 of its unit, so only its first segment is read
+    const bool rec_now = kk == 1 || !pair2;
     if (uniform) {
       // every row of the block belongs to one query: max over the 16 rows first
       float v = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
         const float at_tail0 = __shfl(v, tail0, 16), at15 = __shfl(v, 15, 16);
         const int dfirst_open = kk == 1 && first_open ? cdoc : -2;
         const bool pair_first = kk == 0 ? doc == d0 : doc == dfirst_open;
-        const bool pair_last = rec_now && doc == d15;
+        const bool pair_last = kk == 1 && doc == d15;  // (a pair of one tile has no last segment)
         const bool carried = kk == 0 && cont && doc == d15;
         if (G == 0 && tail && doc >= 0 && !pair_first && !pair_last && !carried)
           a.dsc[(int64_t)rb * a.n_docs + doc] = v;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
         // (rows past n_rows hold unused values)
         const int dfirst_open = kk == 1 && first_open ? cdoc : -2;
         const bool pair_first = kk == 0 ? doc == d0 : doc == dfirst_open;
-        const bool pair_last = rec_now && doc == d15;
+        const bool pair_last = kk == 1 && doc == d15;  // (a pair of one tile has no last segment)
         const bool carried = kk == 0 && cont && doc == d15;
         if (tail && doc >= 0 && !pair_first && !pair_last && !carried)
           reinterpret_cast<float4 *>(a.dsc + ((int64_t)rb * a.n_docs + doc) * 16)[G] = float4{sv[0], sv[1], sv[2], sv[3]};

@@ -493,12 +493,13 @@ def test_layer_degenerate_banks(device, lens, k, t_r):
 # end of the first tile carried into the second): documents of exactly one
 # tile or one pair, documents ending one chunk before or after a tile or pair
 # edge, one-chunk documents, a document crossing from one pair into the next,
-# odd tile counts (a last pair of one tile) and a last tile of one chunk; one
+# odd tile counts (a last pair of one tile, full or partial, whose last
+# documents start inside it) and a last tile of one chunk; one
 # and two row blocks of single-token queries (t_r = 1) and one query per row
 # block (t_r = 16)
 @pytest.mark.parametrize("chunks", [
     [16] * 7, [32] * 3 + [1], [15, 17, 1, 31, 33, 16, 2], [1] * 47, [5, 100, 3, 1], [16, 32, 16], [33],
-    [17, 15], [31, 1, 32, 30, 2, 1]])
+    [17, 15], [31, 1, 32, 30, 2, 1], [16] * 6 + [8, 8], [16] * 6 + [3, 10, 3], [40, 8, 8]])
 @pytest.mark.parametrize("t_r,n_q", [(1, 16), (1, 20), (16, 2)])
 def test_route_pair_units(device, chunks, t_r, n_q):
     base = _wl("prefill-16k")
