@@ -3,6 +3,7 @@
 // include/msa.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -192,15 +193,15 @@ LayerWs layer_ws(const msa_bank *b, int32_t n_q, int32_t T, int32_t t_r, int32_t
 
 namespace msa {
 int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // per device; 0 = not yet queried (calls from several threads are safe)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 }  // namespace msa
 
