@@ -300,25 +300,25 @@ hipError_t layer_tail(const LayerCtx &c, const void *Q, const void *K_loc, const
     msa::RouteArgs ra = route_args(b, nullptr, c.n_q, c.t_r, static_cast<float *>(c.rt_ws()), scores, nullptr,
                                    nullptr);
     // the document scores come from the scan's records and interior scores:
-    // a single-pass top-k completes them as it loads, the sliced one after a
-    // resolve kernel (coalesced over queries)
+    // a single-pass top-k completes them as it loads; over a sliced bank with
+    // small k pass 1 completes them (a few queries per workgroup, adjacent
+    // lanes on adjacent queries) and the attention workgroups make each
+    // query's final selection (two kernels fewer); otherwise a resolve kernel
+    // (coalesced over queries), then the top-k
     msa::TopkSrc src{};
     src.scores = scores;
+    src.mode = msa::TopkSrc::EDGES;
+    src.edges = msa::edge_layout(ra);
+    src.doc_chunk_off = b->doc_chunk_off;
+    src.t_r = c.t_r;
+    n_fused = msa::topk_fused_candidates(b->n_docs, c.k);  // 0 for single-pass banks
     if (msa::topk_single_pass(b->n_docs)) {
-      src.mode = msa::TopkSrc::EDGES;
-      src.edges = msa::edge_layout(ra);
-      src.doc_chunk_off = b->doc_chunk_off;
-      src.t_r = c.t_r;
+      e = msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
+    } else if (n_fused > 0) {
+      e = msa::launch_topk_pass1_resolve(src, c.n_q, b->n_docs, c.k, c.tk_ws(), c.s);
     } else {
       src.mode = msa::TopkSrc::SCORES;
       e = msa::launch_resolve_docs(ra, c.s);
-    }
-    // small k over a sliced bank: pass 1 here, the final selection of each
-    // query inside the attention workgroups (one kernel less)
-    n_fused = msa::topk_single_pass(b->n_docs) ? 0 : msa::topk_fused_candidates(b->n_docs, c.k);
-    if (n_fused > 0) {
-      if (e == hipSuccess) e = msa::launch_topk_pass1(src, c.n_q, b->n_docs, c.k, c.tk_ws(), c.s);
-    } else {
       if (e == hipSuccess) e = msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
     }
     if (e == hipSuccess) e = c.rec(2);

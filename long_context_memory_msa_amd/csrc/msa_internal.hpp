@@ -96,12 +96,11 @@ EdgeLayout edge_layout(const RouteArgs &a);
 // Score of document `doc` for query `q` from a single-writer scan's output:
 // for a document inside one unit the stored score, otherwise the max of its
 // last segment in the first unit it touches and its first segments in the
-// later ones.
-__device__ __forceinline__ float edge_doc_score(const EdgeLayout &L, const int64_t *doc_chunk_off, int n_docs, int t_r,
-                                                int q, int doc) {
+// later ones.  c0 / c1: the document's first and last chunk.
+__device__ __forceinline__ float edge_range_score(const EdgeLayout &L, int n_docs, int t_r, int q, int doc, int64_t c0,
+                                                  int64_t c1) {
   const int rb = t_r == 1 ? q / 16 : q;  // row block of this query
   const int r = t_r == 1 ? q % 16 : 0;   // its row within the block
-  const int64_t c0 = doc_chunk_off[doc], c1 = doc_chunk_off[doc + 1] - 1;
   const int64_t ta = c0 / 32, tb = c1 / 32;
   if (ta == tb && (c0 % 32) != 0 && (c1 % 32) != 31) return L.dsc[((int64_t)rb * n_docs + doc) * L.rw + r];
   const float *rec = L.rec + (int64_t)rb * L.n_units * 32;
@@ -109,6 +108,11 @@ __device__ __forceinline__ float edge_doc_score(const EdgeLayout &L, const int64
   float m = rec[ta * 32 + 16 + r];
   for (int64_t t = ta + 1; t <= tb; ++t) m = fmaxf(m, rec[t * 32 + r]);
   return m;
+}
+
+__device__ __forceinline__ float edge_doc_score(const EdgeLayout &L, const int64_t *doc_chunk_off, int n_docs, int t_r,
+                                                int q, int doc) {
+  return edge_range_score(L, n_docs, t_r, q, doc, doc_chunk_off[doc], doc_chunk_off[doc + 1] - 1);
 }
 
 // ---- top-k -----------------------------------------------------------------
@@ -125,11 +129,14 @@ struct TopkSrc {
 };
 hipError_t launch_topk(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,
                        hipStream_t s);
-// Pass 1 alone (the per-slice candidates, ws as for launch_topk) when the
-// final selection can be left to the attention kernel: returns the number of
-// candidates per query, or 0 when this top-k does not take that form.
+// Whether the final selection can be left to the attention kernel after
+// pass 1 alone (the per-slice candidates, ws as for launch_topk): the number
+// of candidates per query, or 0 when this top-k does not take that form.
 int topk_fused_candidates(int n_docs, int k);
-hipError_t launch_topk_pass1(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s);
+// Pass 1 straight from a single-writer scan's records (EDGES source): one
+// workgroup per (slice, 4 queries) completes the slice's document scores
+// into src.scores and selects each query's k (no separate resolve kernel).
+hipError_t launch_topk_pass1_resolve(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s);
 
 // ---- router projection -------------------------------------------------------
 // Y[rows][out] = X[rows][hidden] W[out][hidden]^T, bf16 in and out, fp32 accumulation;

@@ -335,26 +335,14 @@ constexpr int WS_SLICE = 512;
 constexpr int WS_ITEMS = WS_SLICE / 64;
 constexpr int WS_MAX_K = 32;  // k up to this uses the wave pass (k <= slice / 16)
 
-template <int MODE>
-__global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, int k, int n_slices,
-                                                        uint64_t *cand) {
-  __shared__ __align__(16) uint32_t hist[4][256];
-  const int q = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slice = blockIdx.x * 4 + wave;
-  if (slice >= n_slices) return;  // whole wave; no workgroup barrier below
-  const int lo = slice * WS_SLICE;
-  const int n = std::min(WS_SLICE, n_docs - lo);
+// The wave's k largest of its slice's composites (v[j]: document j * 64 + lane,
+// 0 past the slice) written to out[0, k), padded with zeros.
+__device__ __forceinline__ void wave_slice_select(const uint64_t (&v)[WS_ITEMS], int n, int k, uint32_t *hist,
+                                                  uint64_t *out, int lane) {
   const uint32_t kk = (uint32_t)std::min(k, n);
-  uint64_t v[WS_ITEMS];
-#pragma unroll
-  for (int j = 0; j < WS_ITEMS; ++j) {
-    const int i = j * 64 + lane;  // coalesced
-    v[j] = i < n ? load_composite<MODE>(src, q, n_docs, lo + i) : 0;
-  }
   int shift;
   uint64_t prefix;
-  select_wave<WS_ITEMS>(v, kk, hist[wave], &shift, &prefix);
-  uint64_t *out = cand + ((int64_t)q * n_slices + slice) * k;
+  select_wave<WS_ITEMS>(v, kk, hist, &shift, &prefix);
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < WS_ITEMS; ++j) cnt += (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift));
@@ -369,6 +357,112 @@ __global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, 
   for (int j = 0; j < WS_ITEMS; ++j)
     if (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift)) out[pos++] = v[j];
   for (int j = (int)kk + lane; j < k; j += 64) out[j] = 0;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, int k, int n_slices,
+                                                        uint64_t *cand) {
+  __shared__ __align__(16) uint32_t hist[4][256];
+  const int q = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slice = blockIdx.x * 4 + wave;
+  if (slice >= n_slices) return;  // whole wave; no workgroup barrier below
+  const int lo = slice * WS_SLICE;
+  const int n = std::min(WS_SLICE, n_docs - lo);
+  uint64_t v[WS_ITEMS];
+#pragma unroll
+  for (int j = 0; j < WS_ITEMS; ++j) {
+    const int i = j * 64 + lane;  // coalesced
+    v[j] = i < n ? load_composite<MODE>(src, q, n_docs, lo + i) : 0;
+  }
+  wave_slice_select(v, n, k, hist[wave], cand + ((int64_t)q * n_slices + slice) * k, lane);
+}
+
+// ---- pass 1 from the scan's records, RS_Q queries per workgroup -----------------
+// The workgroup first completes the slice's document scores for its RS_Q
+// queries with the query fastest across lanes (RS_Q lanes read adjacent words
+// of one document's row of stored scores or records and share its chunk-range
+// loads), keeps them in LDS and writes them to src.scores; then wave w selects
+// query q0 + w's k from LDS as the wave pass does.  Measured at 16 queries x
+// 23,048 documents, k = 16: resolve + pass 1 16.0 us as two kernels, 14.0 us
+// fused with RS_Q = 4 (8: 14.2; 16 waves per workgroup: 18.6, four selecting
+// waves per SIMD on a quarter of the CUs); without the batched loads below
+// 20 us.
+constexpr int RS_Q = 4;                           // queries per workgroup
+constexpr int RS_ITEMS = WS_SLICE * RS_Q / (64 * RS_Q);  // documents per thread
+
+// edge_range_score for N documents of one query with their loads batched (a
+// loop per document would wait on each one in turn): the chunk ranges, then
+// each document's stored score or first record, then one round per further
+// 32-chunk unit (loads clamped to the document's last unit, masked after)
+template <int N>
+__device__ __forceinline__ void edge_scores_batched(const EdgeLayout &L, const int64_t *doc_chunk_off, int n_docs,
+                                                    int t_r, int q, const int (&doc)[N], float (&out)[N]) {
+  const int rb = t_r == 1 ? q / 16 : q;
+  const int r = t_r == 1 ? q % 16 : 0;
+  const float *rec = L.rec + (int64_t)rb * L.n_units * 32;
+  int64_t c0[N], c1[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    c0[u] = doc_chunk_off[doc[u]];
+    c1[u] = doc_chunk_off[doc[u] + 1] - 1;
+  }
+  int64_t ta[N], tb[N];
+  int extra = 0;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    ta[u] = c0[u] / 32;
+    tb[u] = c1[u] / 32;
+    const bool one = ta[u] == tb[u];
+    const bool interior = one && (c0[u] % 32) != 0 && (c1[u] % 32) != 31;
+    const float *p = interior ? L.dsc + ((int64_t)rb * n_docs + doc[u]) * L.rw + r
+                              : rec + ta[u] * 32 + ((one && (c0[u] % 32) == 0) ? 0 : 16) + r;
+    out[u] = *p;
+    extra = max(extra, (int)(tb[u] - ta[u]));
+  }
+  for (int e = 1; e <= extra; ++e) {
+    float x[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) x[u] = rec[min(ta[u] + e, tb[u]) * 32 + r];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      if (ta[u] + e <= tb[u]) out[u] = fmaxf(out[u], x[u]);
+  }
+}
+
+__global__ __launch_bounds__(64 * RS_Q) void topk_pass1_resolve(TopkSrc src, int n_q, int n_docs, int k,
+                                                                 int n_slices, uint64_t *cand) {
+  __shared__ float sS[RS_Q][WS_SLICE + 1];
+  __shared__ __align__(16) uint32_t hist[RS_Q][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slice = blockIdx.x, q0 = blockIdx.y * RS_Q;
+  const int lo = slice * WS_SLICE;
+  const int n = std::min(WS_SLICE, n_docs - lo);
+  const int nq = std::min(RS_Q, n_q - q0);
+  const int qq = tid % RS_Q;  // this thread's query; its documents j = u * 64 + tid / RS_Q
+  if (qq < nq) {
+    int doc[RS_ITEMS];
+#pragma unroll
+    for (int u = 0; u < RS_ITEMS; ++u) doc[u] = lo + std::min(u * 64 + tid / RS_Q, n - 1);
+    float sv[RS_ITEMS];
+    edge_scores_batched<RS_ITEMS>(src.edges, src.doc_chunk_off, n_docs, src.t_r, q0 + qq, doc, sv);
+#pragma unroll
+    for (int u = 0; u < RS_ITEMS; ++u) {
+      const int j = u * 64 + tid / RS_Q;
+      if (j < n) {
+        src.scores[(int64_t)(q0 + qq) * n_docs + lo + j] = sv[u];
+        sS[qq][j] = sv[u];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave >= nq) return;  // whole wave; no barrier below
+  uint64_t v[WS_ITEMS];
+#pragma unroll
+  for (int j = 0; j < WS_ITEMS; ++j) {
+    const int i = j * 64 + lane;
+    v[j] = i < n ? composite(score_key(sS[wave][i]), lo + i) : 0;
+  }
+  wave_slice_select(v, n, k, hist[wave], cand + ((int64_t)(q0 + wave) * n_slices + slice) * k, lane);
 }
 
 // ---- pass 2 over register-resident candidates (up to 8 per thread) ----------
@@ -512,22 +606,11 @@ int topk_fused_candidates(int n_docs, int k) {
   return n <= ATTEND_MAX_CAND ? (int)n : 0;
 }
 
-hipError_t launch_topk_pass1(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s) {
+hipError_t launch_topk_pass1_resolve(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s) {
+  if (src.mode != TopkSrc::EDGES || slice_for(k) != WS_SLICE || topk_single_pass(n_docs)) return hipErrorInvalidValue;
   const int ns = n_slices_for(n_docs, k);
-  uint64_t *cand = static_cast<uint64_t *>(ws);
-  switch (src.mode) {
-    case TopkSrc::SCORES:
-      hipLaunchKernelGGL(topk_pass1_wave<TopkSrc::SCORES>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k,
-                         ns, cand);
-      break;
-    case TopkSrc::KEYS:
-      hipLaunchKernelGGL(topk_pass1_wave<TopkSrc::KEYS>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k, ns,
-                         cand);
-      break;
-    default:
-      hipLaunchKernelGGL(topk_pass1_wave<TopkSrc::EDGES>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k,
-                         ns, cand);
-  }
+  hipLaunchKernelGGL(topk_pass1_resolve, dim3(ns, (n_q + RS_Q - 1) / RS_Q), dim3(64 * RS_Q), 0, s, src, n_q, n_docs,
+                     k, ns, static_cast<uint64_t *>(ws));
   return hipGetLastError();
 }
 

@@ -415,15 +415,34 @@ def test_layer_halves_equal_layer_forward(device, name, t_r):
 @pytest.mark.parametrize("k", [16, 32])
 def test_layer_sliced_topk_selected_in_attention(device, k):
     # more documents than one top-k workgroup holds (8,192), small k: the layer
-    # runs top-k pass 1 only and every attention workgroup selects its
-    # query's documents from the candidates itself; it must equal the
-    # separate route / top-k / attend calls bit for bit, and the oracle
+    # runs top-k pass 1 only (completing the document scores from the scan's
+    # records itself) and every attention workgroup selects its query's
+    # documents from the candidates; it must equal the separate route / top-k
+    # / attend calls bit for bit, and the oracle
     g = np.random.default_rng(11)
     lens = g.integers(8, 41, size=9_000).astype(np.int64)  # one chunk per document
     w = _wl("decode-100m", 200_000, doc_lens=lens, chunk=64, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, n_q=4, k=k, pos0=k,
             gold=np.zeros((4, 0), dtype=np.int64))
     assert w.n_docs > 8192 and w.n_chunks == w.n_docs
-    log(f"sliced layer k={k}: docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q}")
+    _check_sliced_layer(w, device)
+
+
+@pytest.mark.parametrize("n_q,t_r", [(20, 1), (3, 4)])
+def test_layer_sliced_multi_unit_documents(device, n_q, t_r):
+    # the same sliced layer with documents of 1-4 chunks and, every 500th, one
+    # of 40 chunks crossing 32-chunk units; 20 single-token queries (a second,
+    # partial block of 16) and 3 queries of 4 router tokens (a row block each)
+    g = np.random.default_rng(12 + n_q)
+    lens = g.integers(1, 65, size=8_400).astype(np.int64)
+    lens[::500] = 40 * 16 - 3
+    w = _wl("decode-100m", 200_000, doc_lens=lens, chunk=16, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, n_q=n_q, k=16,
+            pos0=16, T_route=t_r, L_loc=t_r, gold=np.zeros((n_q, 0), dtype=np.int64))
+    assert w.n_docs > 8192 and w.n_chunks > 2 * w.n_docs
+    _check_sliced_layer(w, device)
+
+
+def _check_sliced_layer(w, device):
+    log(f"sliced layer k={w.k}: docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q} t_r={w.T_route}")
     qi, K, V, KR = host_inputs(w)
     ob = oracle_bank(w, K, V, KR)
     bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
