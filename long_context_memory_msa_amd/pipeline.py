@@ -22,7 +22,8 @@ the room they leave.  Measured at the 100M-token decode workload: one route
 stream with the full grid 308-312 us per step, two route streams with capped
 grids 294-296 us (one route stream, capped: 310 us; three route streams:
 297-305 us; the route/select-attend layer halves on two route streams:
-300-309 us).
+300-309 us, and 284-292 us with their scan capped too, which takes the
+resolve kernel off the route streams).
 
 The pages load the selected documents' pooled rows asynchronously while the
 search goes on (hotdry blog, key engineering details: tiered storage and
