@@ -387,8 +387,10 @@ __global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, 
 // fused with RS_Q = 4 (8: 14.2; 16 waves per workgroup: 18.6, four selecting
 // waves per SIMD on a quarter of the CUs); without the batched loads below
 // 20 us.
-constexpr int RS_Q = 4;                           // queries per workgroup
-constexpr int RS_ITEMS = WS_SLICE * RS_Q / (64 * RS_Q);  // documents per thread
+constexpr int RS_Q = 4;                    // queries per workgroup (one selecting wave each)
+constexpr int RS_ITEMS = WS_SLICE / 64;    // documents per thread: j = u * 64 + tid / RS_Q
+static_assert(RS_Q <= 16 && 16 % RS_Q == 0, "a workgroup's queries share one 16-query row block");
+static_assert(RS_ITEMS == WS_ITEMS, "the resolve and the selection cover the same slice");
 
 // edge_range_score for N documents of one query with their loads batched (a
 // loop per document would wait on each one in turn): the chunk ranges, then
