@@ -31,9 +31,14 @@ Readings taken where the pages are silent:
   R10 the router projectors are plain linear maps without bias (Q^R = x W_QR^T,
      K^R = h W_KR^T per token, before pooling); their outputs are stored in
      the bank dtype (rounded once) like every other stored tensor.
+  R11 Memory Interleave: round r routes with every active token of the layer
+     (T0 + append * r), then attends only the tokens new in that round (T0,
+     then ``append``) over the selected documents plus the whole causal local
+     context; local token s stays at global position pos0 + s in every round.
 
-Parity is pinned for every function by tests/test_oracle_pins.py; none is
-"parity unpinned".
+Parity is pinned for every function by tests/test_oracle_pins.py (interleave
+by the hand-derived tests/golden/interleave_tiny.json and by its slices and
+positions); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -318,7 +323,8 @@ def interleave(layers: Sequence[Dict[str, np.ndarray]], banks: Sequence[Dict[str
     round are the next ``append`` rows.  Round r routes with every active
     token (T0 + append * r), then attends the tokens new in that round (T0 in
     round 0, ``append`` afterwards) over the selected documents plus the full
-    causal local context.  Returns results[r][l] = layer_forward output.
+    causal local context (reading R11).  Returns results[r][l] =
+    layer_forward output.
     """
     out = []
     for r in range(rounds):

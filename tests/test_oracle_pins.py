@@ -376,3 +376,91 @@ def test_project_is_linear_and_batches_leading_axes():
     Wz = Wt.copy()
     Wz[5] = 0.0
     assert np.all(O.project(X1, Wz)[..., 5] == 0.0)
+
+
+# ---- Memory Interleave (hotdry blog, sparse strategy and parameters; Lighthouse
+# digest, Component 3) ----------------------------------------------------------
+def _interleave_fixture():
+    with open(os.path.join(GOLDEN, "interleave_tiny.json")) as f:
+        g = json.load(f)
+    bank = {name: np.array(g[name], dtype=np.float64) for name in ("krbar", "kbar", "vbar")}
+    bank["doc_chunk_off"] = np.array(g["doc_chunk_off"], dtype=np.int64)
+    layer = {name: np.array(g[name], dtype=np.float64) for name in ("QR", "Q", "K_loc", "V_loc")}
+    return g, bank, layer
+
+
+def test_interleave_golden_fixture():
+    # hand-derived two-round example: round 1 re-routes with all active tokens
+    # (the new token alone would pick [C, B], no re-routing [A, B]), attends only
+    # the new token at position pos0 + 1 over the whole causal local context
+    g, bank, layer = _interleave_fixture()
+    res = O.interleave([layer], [bank], g["T0"], g["append"], g["rounds"], g["k"], g["pos0"], scale=g["scale"])
+    assert len(res) == g["rounds"] == 2 and all(len(r) == 1 for r in res)
+    for r, want in enumerate(g["rounds_expected"]):
+        got = res[r][0]
+        assert np.allclose(got["s_doc"], want["s_doc"], atol=1e-15, rtol=0), r
+        assert got["idx"].tolist() == want["idx"], r
+        assert np.allclose(got["val"], want["val"], atol=1e-15, rtol=0), r
+        assert np.allclose(got["gap"], want["gap"], atol=1e-15, rtol=0), r
+        assert got["O"].shape == np.array(want["O"]).shape, r          # only the new token is attended
+        assert np.allclose(got["O"], want["O"], atol=1e-15, rtol=0), r
+
+
+def test_interleave_rounds_route_all_active_tokens_and_attend_the_new_ones(monkeypatch):
+    # every layer call of every round sees exactly: router tokens [0, L_act),
+    # query tokens [L_act - T_new, L_act), local context [0, L_act), its own
+    # layer's bank, the same k and pos0 -- recorded at the layer_forward boundary
+    from oracle import msa_oracle as MO
+
+    T0, append, rounds, k, pos0, n_layers = 5, 2, 3, 2, 2, 2
+    L = T0 + append * (rounds - 1)
+    layers = [{"QR": _rand((1, L, 2, 4), 200 + 4 * li), "Q": _rand((1, L, 4, 4), 201 + 4 * li),
+               "K_loc": _rand((1, L, 2, 4), 202 + 4 * li), "V_loc": _rand((1, L, 2, 4), 203 + 4 * li)}
+              for li in range(n_layers)]
+    banks = [_bank(210 + li, [3, 5, 2, 7], 2, 4, chunk=2) for li in range(n_layers)]
+    for li, b in enumerate(banks):
+        b["krbar"] = _rand((b["kbar"].shape[1], 2, 4), 220 + li)
+    calls = []
+    real = MO.layer_forward
+
+    def spy(QR, Q, K_loc, V_loc, bank, k_, pos0_, scale=None, base=10000.0):
+        calls.append((QR, Q, K_loc, V_loc, bank, k_, pos0_))
+        return real(QR, Q, K_loc, V_loc, bank, k_, pos0_, scale, base)
+
+    monkeypatch.setattr(MO, "layer_forward", spy)
+    out = MO.interleave(layers, banks, T0, append, rounds, k, pos0)
+    assert len(calls) == rounds * n_layers
+    for r in range(rounds):
+        L_act, T_new = T0 + append * r, (T0 if r == 0 else append)
+        for li in range(n_layers):
+            QR, Q, K_loc, V_loc, bank, k_, pos0_ = calls[r * n_layers + li]
+            inp = layers[li]
+            assert np.array_equal(QR, inp["QR"][:, :L_act]), (r, li)
+            assert np.array_equal(Q, inp["Q"][:, L_act - T_new:L_act]), (r, li)
+            assert np.array_equal(K_loc, inp["K_loc"][:, :L_act]) and np.array_equal(V_loc, inp["V_loc"][:, :L_act])
+            assert bank is banks[li] and k_ == k and pos0_ == pos0
+            assert out[r][li]["O"].shape == (1, T_new, 4, 4)
+
+
+def test_interleave_rounds_equal_one_causal_prefill_on_their_selection():
+    # positions continue across rounds: the tokens new in round r, attended over
+    # that round's selection, equal the same rows of one causal prefill of all
+    # L_act tokens (local token s at position pos0 + s in both) -- a token
+    # placed at pos0 + t of its round, or seeing only the new tokens' local
+    # keys, would differ
+    T0, append, rounds, k, pos0 = 4, 3, 3, 2, 2
+    L = T0 + append * (rounds - 1)
+    inp = {"QR": _rand((1, L, 2, 4), 230), "Q": _rand((1, L, 4, 4), 231),
+           "K_loc": _rand((1, L, 2, 4), 232), "V_loc": _rand((1, L, 2, 4), 233)}
+    bank = _bank(234, [3, 5, 2, 7, 4], 2, 4, chunk=2)
+    bank["krbar"] = _rand((bank["kbar"].shape[1], 2, 4), 235)
+    out = O.interleave([inp], [bank], T0, append, rounds, k, pos0)
+    for r in range(rounds):
+        L_act, T_new = T0 + append * r, (T0 if r == 0 else append)
+        idx = out[r][0]["idx"]
+        full = O.attend(inp["Q"][:, :L_act], inp["K_loc"][:, :L_act], inp["V_loc"][:, :L_act], bank["kbar"],
+                        bank["vbar"], bank["doc_chunk_off"], idx, pos0)
+        assert np.allclose(out[r][0]["O"], full[:, L_act - T_new:], atol=1e-13, rtol=0), r
+        # and the selection is the top-k of the routing over all L_act tokens
+        s = O.doc_scores(O.chunk_scores(inp["QR"][:, :L_act], bank["krbar"]), bank["doc_chunk_off"])
+        assert np.array_equal(idx, O.topk(s, k)["idx"]), r
