@@ -32,7 +32,9 @@ def interleave(banks: Sequence[Bank], rope: Rope, layers: Sequence[Dict[str, tor
     ``layers[l]`` holds device tensors Q [n_q][L][h_q][d], K_loc / V_loc
     [n_q][L][h_kv][d] and QR [n_q][L][h_r][d_r] over the whole context
     (L >= T0 + append * (rounds - 1)).  Returns out[r][l] = {O, idx, val
-    [, s_doc]}.
+    [, s_doc]}.  Every copy, allocation and layer call runs on ``stream`` (a
+    torch.cuda.Stream; None = the current stream): the caller orders the
+    writes of ``layers`` before it and its uses of the outputs after it.
     """
     if not banks or len(banks) != len(layers):
         raise ValueError("one bank per layer is required")
@@ -45,6 +47,18 @@ def interleave(banks: Sequence[Bank], rope: Rope, layers: Sequence[Dict[str, tor
     nb = max(_lib.msa_layer_workspace_bytes(b.c, n_q, T0 if r == 0 else append, T0 + append * r, T0 + append * r,
                                             h_q, k)
              for b in banks for r in range(rounds))
+    # the copies of strided slices and the output tensors are made on the
+    # stream the layer calls run on, so that the allocator and the kernels see
+    # one order of work
+    strm = torch.cuda.current_stream(dev) if stream is None else stream
+    if not isinstance(strm, torch.cuda.Stream):
+        raise TypeError("stream must be a torch.cuda.Stream (or None for the current stream)")
+    with torch.cuda.stream(strm):
+        return _rounds(banks, rope, layers, T0, append, rounds, k, pos0, h_q, scale, want_scores, strm, nb, n_q, d,
+                       dev, td)
+
+
+def _rounds(banks, rope, layers, T0, append, rounds, k, pos0, h_q, scale, want_scores, stream, nb, n_q, d, dev, td):
     ws = workspace(nb, dev)
     out = []
     for r in range(rounds):

@@ -89,12 +89,26 @@ def assert_attention_close(got: np.ndarray, want: np.ndarray, max_abs: float = 2
 
 
 def topk_set_valid(gpu_idx: np.ndarray, s_oracle: np.ndarray, k: int, slack: float = 4e-3) -> None:
-    """Every selected document scores within ``slack`` of the oracle's k-th best; no repeats."""
+    """A top-k selection made on the GPU's own scores, against the oracle's
+    scores: k distinct documents, each scoring at least the oracle's k-th best
+    minus ``slack``, and every document that scores more than the k-th best
+    plus ``slack`` (a clear winner) among them."""
     for q in range(gpu_idx.shape[0]):
         row = gpu_idx[q]
-        assert len(set(row.tolist())) == k
+        assert len(set(row.tolist())) == k and np.all((row >= 0) & (row < s_oracle.shape[1])), (q, row)
         kth = np.sort(s_oracle[q])[::-1][k - 1]
         assert np.all(s_oracle[q, row] >= kth - slack), (q, row, kth)
+        winners = np.flatnonzero(s_oracle[q] > kth + slack)
+        assert set(winners.tolist()) <= set(row.tolist()), (q, winners, row)
+
+
+def check_topk_property(s_doc: np.ndarray, idx: np.ndarray, val: np.ndarray, k: int) -> None:
+    """idx is the first k of the (descending score, ascending index) order of
+    the GPU's own s_doc, and val the scores of those documents (bit-exact)."""
+    for q in range(s_doc.shape[0]):
+        order = np.lexsort((np.arange(s_doc.shape[1]), -s_doc[q].astype(np.float64)))[:k]
+        assert idx[q].tolist() == order.tolist(), q
+        assert np.array_equal(val[q], s_doc[q, idx[q]])
 
 
 def run_layer(bank, rope, w: W.Workload, QR, Q, K_loc, V_loc, device, events=None):

@@ -11,7 +11,9 @@ times.
 * 18 routed layers x 10M tokens with 3 Memory Interleave rounds (interleave-10mx18):
   per-layer banks on the GPU, the interleave driver, sampled pooled rows and
   router scores for sampled layers and rounds, top-k properties everywhere,
-  and full-shape attention (prefill and a later round) against the oracle.
+  the attention of sampled layers in every round on the layer's own selection,
+  and full-shape attention (prefill and a later round) on test-chosen
+  documents, all against the oracle.
 Tolerances as in test_gpu_parity.py.
 """
 import numpy as np
@@ -23,7 +25,7 @@ from synth import device as sdev, rng, workloads as W
 from long_context_memory_msa_amd import _lib as L, memory as M, offline
 from long_context_memory_msa_amd.interleave import interleave
 
-from gpu_common import assert_attention_close, bf16_spacing, dev, host, log
+from gpu_common import assert_attention_close, bf16_spacing, check_topk_property, dev, host, log, topk_set_valid
 
 pytestmark = pytest.mark.gpu
 
@@ -78,14 +80,6 @@ def check_pooled_rows(w, bank, ob_docs):
     return n
 
 
-def check_topk_property(s_doc, idx, val, k):
-    """idx is the first k of the (descending score, ascending index) order of s_doc."""
-    for q in range(s_doc.shape[0]):
-        order = np.lexsort((np.arange(s_doc.shape[1]), -s_doc[q].astype(np.float64)))[:k]
-        assert idx[q].tolist() == order.tolist(), q
-        assert np.array_equal(val[q], s_doc[q, idx[q]])
-
-
 def compact_bank(ob_docs, docs):
     """A bank of just ``docs`` (in that order) built from per-document oracle pools."""
     kbar = np.concatenate([ob_docs[d]["kbar"] for d in docs], axis=1)
@@ -130,8 +124,12 @@ def test_full_1m_bank_layer(device):
     check_topk_property(s_doc.cpu().numpy(), gi, val.cpu().numpy(), w.k)
     if want["gap"][0] > 4e-3:
         assert set(gi[0].tolist()) == set(want["idx"][0].tolist())
-    if set(gi[0].tolist()) == set(want["idx"][0].tolist()):
-        assert_attention_close(host(out), want["O"])
+    topk_set_valid(gi, want["s_doc"], w.k)
+    # the layer's attention against the oracle's over the layer's own selection
+    o_ref = O.attend(qi["Q"][:, :w.L_loc], qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], ob["kbar"],
+                     ob["vbar"], ob["doc_chunk_off"], gi, w.pos0, base=w.rope_base)
+    e = assert_attention_close(host(out), o_ref)
+    log(f"  attention on the layer's own selection: max {e[0]:.3g} mean {e[1]:.3g}")
 
 
 # ---------------------------------------------------------------------------
@@ -225,7 +223,23 @@ def test_full_interleave_18_layers(device):
             for doc in docs:
                 S = O.chunk_scores(hosts[layer]["QR"][:, :L_act], ob_docs[doc]["krbar"])
                 assert np.abs(sd[:, doc] - S.max(axis=1)).max() <= 2e-3, (layer, r, doc)
-    # full-shape attention against the oracle: prefill (round 0) and the last round
+    # every round of sampled layers: the layer's attention on its own selection
+    # against the oracle's (pooled rows of the selected documents regenerated
+    # from the counter generator)
+    for layer in (0, 7, w.n_layers - 1):
+        qi = hosts[layer]
+        for r in range(w.rounds):
+            L_act = w.L_loc + w.append * r
+            T_new = w.L_loc if r == 0 else w.append
+            sel = [int(x) for x in res[r][layer]["idx"].cpu().numpy()[0]]
+            obs = oracle_docs(w, sel, layer, None)
+            kbar, vbar, off = compact_bank(obs, sel)
+            want = O.attend(qi["Q"][:, L_act - T_new:L_act], qi["K_loc"][:, :L_act], qi["V_loc"][:, :L_act], kbar,
+                            vbar, off, np.arange(w.k)[None, :], w.pos0, base=w.rope_base)
+            e = assert_attention_close(host(res[r][layer]["O"]), want)
+            log(f"  layer {layer} round {r}: attention on its own selection, max {e[0]:.3g} mean {e[1]:.3g}")
+    # full-shape attention against the oracle on test-chosen documents: prefill
+    # (round 0) and the last round
     layer = 3
     sel = [int(x) for x in np.random.default_rng(9).choice(w.n_docs, size=w.k, replace=False)]
     obs = oracle_docs(w, sel, layer, None)
