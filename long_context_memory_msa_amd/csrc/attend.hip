@@ -29,17 +29,13 @@
 namespace msa {
 namespace {
 
-// Split heuristics (compile-time knobs): splits target SPLIT_MUL waves per
-// CU in total, with at least MIN_TILES key tiles per split.  (Counting waves,
+// Split heuristics: splits target SPLIT_MUL waves per CU in total, with at
+// least MIN_TILES key tiles per split.  (Counting waves,
 // not workgroups: prefill with 4-wave workgroups already fills the GPU and
 // every further split only adds merge traffic -- 512 query tokens 56 -> 44
 // us; 64 tokens 25 -> 21 us; decode unchanged.)
-#ifndef MSA_ATTEND_SPLIT_MUL
-#define MSA_ATTEND_SPLIT_MUL 4
-#endif
-#ifndef MSA_ATTEND_MIN_TILES
-#define MSA_ATTEND_MIN_TILES 2
-#endif
+constexpr int SPLIT_MUL = 4;
+constexpr int MIN_TILES = 2;
 
 constexpr int KT = 32;          // keys per tile
 constexpr int MAX_K = 256;      // selected documents per query
@@ -462,8 +458,8 @@ Plan plan(const AttendArgs &a) {
   // workgroup per (query, KV head, row group) keeps enough rows in flight
   // while leaving the GPU to a concurrent router scan
   const int64_t waves = base * p.wgw;
-  int64_t ns = a.kv_host ? 1 : ((int64_t)MSA_ATTEND_SPLIT_MUL * device_cu_count() + waves - 1) / waves;
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / MSA_ATTEND_MIN_TILES));
+  int64_t ns = a.kv_host ? 1 : ((int64_t)SPLIT_MUL * device_cu_count() + waves - 1) / waves;
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / MIN_TILES));
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, 64));
   p.n_split = (int)ns;
   return p;

@@ -17,10 +17,6 @@
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
-// 1 = the bf16 piece-wise pooling kernel where the shapes allow it
-#ifndef MSA_POOL_PIECES
-#define MSA_POOL_PIECES 1
-#endif
 
 namespace msa {
 namespace {
@@ -301,7 +297,7 @@ hipError_t launch_pool(const PoolArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.chunk_end <= a.chunk_begin) return hipSuccess;
-  if (MSA_POOL_PIECES && pool_pieces_ok(a)) return pool_pieces_dispatch(a, s);
+  if (pool_pieces_ok(a)) return pool_pieces_dispatch(a, s);
   return a.dtype == 0 ? pool_dispatch<float>(a, s) : pool_dispatch<bf16_t>(a, s);
 }
 

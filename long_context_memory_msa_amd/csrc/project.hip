@@ -38,10 +38,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int PT = 128;  // rows (and outputs) per workgroup
 constexpr int SK = 64;   // K elements per stage
 // row counts up to this take the skinny kernel (at most 4 row tiles of 16)
-#ifndef MSA_PROJ_SKINNY_ROWS
-#define MSA_PROJ_SKINNY_ROWS 64
-#endif
-constexpr int SKINNY_ROWS = MSA_PROJ_SKINNY_ROWS;
+constexpr int SKINNY_ROWS = 64;
 static_assert(SKINNY_ROWS <= 64, "skinny projection holds at most 4 row tiles");
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }

@@ -39,46 +39,17 @@
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
-// Tuning knobs (compile-time): prefetch depth in heads, and whether the key
-// stream uses non-temporal loads.
-#ifndef MSA_ROUTE_PD
+// Prefetch depth of the key stream in heads, and the waves per SIMD the scan
+// kernels are compiled for (launch bounds).
 #define MSA_ROUTE_PD 2
-#endif
-#ifndef MSA_ROUTE_NT
-#define MSA_ROUTE_NT 0
-#endif
-// workgroups per CU in the persistent grid (0 = as many as stay resident)
-#ifndef MSA_ROUTE_WGCU
-#define MSA_ROUTE_WGCU 0
-#endif
-// 1 = query fragments held in VGPRs, 0 = re-read from LDS each step
-#ifndef MSA_ROUTE_QREG
-#define MSA_ROUTE_QREG 0
-#endif
-#ifndef MSA_ROUTE_WAVES
 #define MSA_ROUTE_WAVES 3
-#endif
-// 1 = size the persistent grid so that every wave gets the same number of tiles
-#ifndef MSA_ROUTE_BALANCE
-#define MSA_ROUTE_BALANCE 1
-#endif
 
 namespace msa {
 namespace {
 
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::type load_stream(const T *p) {
-#if MSA_ROUTE_NT
-  if constexpr (sizeof(T) == 2) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return __builtin_bit_cast(bf16x8, v);
-  } else {
-    return __builtin_nontemporal_load(p);
-  }
-#else
   return load_frag<T>(p);
-#endif
 }
 
 __global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t v) {
@@ -213,14 +184,7 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
   }
   __syncthreads();
 
-#if MSA_ROUTE_QREG
-  FT qreg[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) qreg[f] = qfrag[f][lane];
-#define MSA_QOP(f) qreg[f]
-#else
 #define MSA_QOP(f) qfrag[(f) + zoff][lane]
-#endif
 
   // single writer: a record per pair of tiles (a 32-chunk unit); the open
   // document of the pair's first tile is carried into its second
@@ -245,12 +209,10 @@ __global__ __launch_bounds__(256, MSA_ROUTE_WAVES) void route_scan_kernel(RouteA
     // moments earlier, so they are served by L2 rather than HBM)
     kp_nxt = krbar + lane_chunk(tile_pf) * (HR * DR) + G * EL + (has_next ? 0 : (HR - PD) * DR);
     load_meta(tile_pf, ik_nxt, doc_nxt);
-#if !MSA_ROUTE_QREG
     // opaque zero: keeps the query-fragment LDS reads inside the loop rather
     // than hoisting all of Q into VGPRs (registers go to the prefetch ring)
     int zoff;
     asm volatile("s_mov_b32 %0, 0" : "=s"(zoff));
-#endif
     f32x4 S = zero4();
 #pragma unroll
     for (int h = 0; h < HR; ++h) {
@@ -456,7 +418,7 @@ ScanGrid grid_of(const RouteArgs &a) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, route_scan_kernel<T, HR, DR, EDGE>, 256, 0) != hipSuccess ||
         n < 1)
       n = 1;
-    res = MSA_ROUTE_WGCU > 0 && MSA_ROUTE_WGCU < n ? MSA_ROUTE_WGCU : n;
+    res = n;
     resident.store(res, std::memory_order_relaxed);
   }
   // a caller that runs other kernels beside the scan (a pipelined decode step)
@@ -469,7 +431,6 @@ ScanGrid grid_of(const RouteArgs &a) {
   const int64_t slots = (int64_t)device_cu_count() * per_cu;  // resident workgroups
   int64_t wgs = std::max<int64_t>(1, slots / rbs);
   wgs = std::max<int64_t>(1, std::min<int64_t>(wgs, (n_tiles + 3) / 4));
-#if MSA_ROUTE_BALANCE
   // Balance: as few waves as still need the same number of rounds of tiles,
   // so that no small set of waves finishes a last, partial round alone at a
   // fraction of the bandwidth.  (Counted in tiles although the waves take
@@ -480,7 +441,6 @@ ScanGrid grid_of(const RouteArgs &a) {
     const int64_t rounds = (n_tiles + 4 * wgs - 1) / (4 * wgs);
     wgs = (n_tiles + 4 * rounds - 1) / (4 * rounds);
   }
-#endif
   ScanGrid g;
   g.wgs = wgs;
   g.n_waves = wgs * 4;  // wave w starts at tile w

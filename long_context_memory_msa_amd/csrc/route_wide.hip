@@ -39,11 +39,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int MW = 128;  // rows per workgroup
-// chunks per workgroup (a compile-time knob: 128 -> 4 waves, 256 -> 8 waves)
-#ifndef MSA_WIDE_NW
-#define MSA_WIDE_NW 128
-#endif
-constexpr int WIDE_NW = MSA_WIDE_NW;
+constexpr int WIDE_NW = 128;  // chunks per workgroup (4 waves of 64 x 64)
 
 // qinv[h][row] = (1/H_r) / ||Q^R[row][h]|| (0 for a zero row); 16 lanes per
 // (row, head).  Also zeroes zero[0, n_zero) (the document keys the scan maxes

@@ -41,10 +41,8 @@ struct SelShared {
   uint32_t in_bin;   // elements in the chosen bin
 };
 
-// Single-pass limit (documents per query), a compile-time knob.
-#ifndef MSA_TOPK_SINGLE_MAX
-#define MSA_TOPK_SINGLE_MAX 8192
-#endif
+// Single-pass limit (documents per query).
+constexpr int TOPK_SINGLE_MAX = 8192;
 
 // Exclusive prefix sum over the block; returns this thread's offset, *total.
 __device__ int block_excl_scan(int v, SelShared &sh, int *total) {
@@ -565,7 +563,7 @@ int n_slices_for(int n_docs, int k) { return (n_docs + slice_for(k) - 1) / slice
 
 }  // namespace
 
-bool topk_single_pass(int n_docs) { return n_docs <= TS_THREADS * TS_ITEMS && n_docs <= MSA_TOPK_SINGLE_MAX; }
+bool topk_single_pass(int n_docs) { return n_docs <= TS_THREADS * TS_ITEMS && n_docs <= TOPK_SINGLE_MAX; }
 
 size_t topk_ws_bytes(int n_q, int n_docs, int k) {
   if (topk_single_pass(n_docs)) return 0;
@@ -597,13 +595,9 @@ hipError_t topk_launch(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *
   return hipGetLastError();
 }
 
-// 1 = the layer leaves the final selection to the attention kernel where it can
-#ifndef MSA_TOPK_FUSE
-#define MSA_TOPK_FUSE 1
-#endif
-
+// The layer leaves the final selection to the attention kernel where it can.
 int topk_fused_candidates(int n_docs, int k) {
-  if (!MSA_TOPK_FUSE || topk_single_pass(n_docs) || slice_for(k) != WS_SLICE) return 0;
+  if (topk_single_pass(n_docs) || slice_for(k) != WS_SLICE) return 0;
   const int64_t n = (int64_t)n_slices_for(n_docs, k) * k;
   return n <= ATTEND_MAX_CAND ? (int)n : 0;
 }
