@@ -8,15 +8,13 @@ from __future__ import annotations
 
 import ctypes
 import math
-import os
 from pathlib import Path
 from typing import Optional, Sequence
 
 import numpy as np
 
 _HERE = Path(__file__).resolve().parent
-# MSA_LIBRARY selects another build of the same library (e.g. a tuning variant)
-LIB_PATH = Path(os.environ["MSA_LIBRARY"]) if os.environ.get("MSA_LIBRARY") else _HERE / "libmsa.so"
+LIB_PATH = _HERE / "libmsa.so"
 
 MSA_OK, MSA_ERR_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(5)
 MSA_F32, MSA_BF16 = 0, 1

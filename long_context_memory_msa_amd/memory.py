@@ -87,22 +87,22 @@ class Bank:
         lens = np.asarray(doc_lens, dtype=np.int64)
         if lens.size == 0:
             return self.n_docs, self.n_docs
-        if (lens < 1).any():
-            raise ValueError("document lengths must be >= 1")
+        # the new documents' own layout (the library's helper validates the
+        # lengths), shifted to the end of the bank
+        lay = _lib.msa_bank_layout(lens, self.chunk)
         n0, c0 = self.n_docs, self.n_chunks
-        nch = (lens + self.chunk - 1) // self.chunk
-        n1, c1 = n0 + lens.size, c0 + int(nch.sum())
+        n1, c1 = n0 + lens.size, c0 + lay["n_chunks"]
         if n1 > self.cap_docs or c1 > self.cap_chunks:
             raise ValueError(f"bank capacity exceeded: {n1} documents / {c1} chunks "
                              f"(capacity {self.cap_docs} / {self.cap_chunks})")
-        self.doc_tok_off_host[n0 + 1:n1 + 1] = self.doc_tok_off_host[n0] + np.cumsum(lens)
-        self.doc_chunk_off_host[n0 + 1:n1 + 1] = c0 + np.cumsum(nch)
+        self.doc_tok_off_host[n0 + 1:n1 + 1] = self.doc_tok_off_host[n0] + lay["doc_tok_off"][1:]
+        self.doc_chunk_off_host[n0 + 1:n1 + 1] = c0 + lay["doc_chunk_off"][1:]
         self.doc_tok_off[n0 + 1:n1 + 1].copy_(torch.from_numpy(self.doc_tok_off_host[n0 + 1:n1 + 1]))
         self.doc_chunk_off[n0 + 1:n1 + 1].copy_(torch.from_numpy(self.doc_chunk_off_host[n0 + 1:n1 + 1]))
         self.n_docs, self.n_chunks = n1, c1
         self.c.n_docs, self.c.n_chunks = n1, c1
-        self.c.max_doc_len = max(int(self.c.max_doc_len), int(lens.max()))
-        self.c.max_doc_chunks = (self.c.max_doc_len + self.chunk - 1) // self.chunk
+        if lay["max_doc_len"] > self.c.max_doc_len:
+            self.c.max_doc_len, self.c.max_doc_chunks = lay["max_doc_len"], lay["max_doc_chunks"]
         return n0, n1
 
     @property

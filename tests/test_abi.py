@@ -119,8 +119,9 @@ def test_bank_capacity_host_side():
     assert b.append([]) == (5, 5)
     with pytest.raises(ValueError):
         b.append([129])          # 2 more chunks > capacity 12
-    with pytest.raises(ValueError):
-        b.append([0])
+    with pytest.raises(msa.MsaError) as e:
+        b.append([0])            # lengths are validated by the library's layout helper
+    assert e.value.code == L.MSA_ERR_ARG and (b.n_docs, b.n_chunks) == (5, 11)
     assert isinstance(b.kbar, torch.Tensor)
 
 
