@@ -288,6 +288,27 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
                       size_t ws_bytes, void *const *stage_events, void *stream);
 
 /*
+ * msa_layer_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace taken from a static device
+ * array of MSA_STATIC_WORKSPACE_BYTES that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates nothing.  It serves
+ * every layer whose msa_layer_workspace_bytes is at most that size (the
+ * 100M-token decode layer of 16 single-token queries and k = 16 needs about
+ * 8 MiB); larger ones fail with MSA_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's array (the kernels reset whatever
+ * must start from zero): calls that overlap on one GPU, on any streams, race
+ * and must be serialised by the caller.  The first call on a device looks up
+ * the array's address there (no allocation).  Arguments, outputs and errors as
+ * msa_layer_forward.
+ */
+#define MSA_STATIC_WORKSPACE_BYTES (16u << 20)
+int msa_layer_forward_noalloc(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,
+                              int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0,
+                              float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc,
+                              void *const *stage_events, void *stream);
+
+/*
  * The two halves of msa_layer_forward, for callers that overlap independent
  * batches (the router scan of one batch streams the bank while the top-k and
  * attention of the previous one run on another stream -- the pages overlap

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/msa.h"
@@ -349,6 +350,33 @@ hipError_t layer_tail(const LayerCtx &c, const void *Q, const void *K_loc, const
   return e;
 }
 
+// Workspace of msa_layer_forward_noalloc: one array per GPU in the code
+// object's device memory, alive until the process ends.  Host code never
+// passes `scratch` itself to a kernel or a copy (on the host it names a
+// stand-in, not the device array): it uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on the first call there.
+static __device__ __align__(256) unsigned char scratch[MSA_STATIC_WORKSPACE_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_addr[64] = {};  // per device; null = not looked up yet
+
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MSA_ERR_UNSUPPORTED, "device %d (the static workspace serves devices 0-63)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return dev_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -609,23 +637,71 @@ size_t msa_layer_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int3
   return layer_ws(b, n_q, T, t_r, L_loc, h_q, k).total;
 }
 
+// The whole layer (validated except for the workspace, whose pointer and size
+// the caller has checked) on `stream`.
+int layer_forward_checked(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,
+                          int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0,
+                          float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
+                          void *const *stage_events, void *stream) {
+  const LayerCtx c{b, n_q, T, t_r, L_loc, h_q, k, static_cast<char *>(ws), layer_ws(b, n_q, T, t_r, L_loc, h_q, k),
+                   (hipStream_t)stream, stage_events};
+  hipError_t e = layer_route(c, QR, s_doc);
+  if (e == hipSuccess) e = layer_tail(c, Q, K_loc, V_loc, pos0, scale, rope, O, idx, val, s_doc);
+  return e == hipSuccess ? ok() : dev_fail(e, "layer_forward");
+}
+
+// Validation of a whole layer call; check_ws = false leaves out the workspace
+// (the caller checks its own).
+int check_layer(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR, int32_t n_q,
+                int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0, float scale,
+                const msa_rope *rope, const void *O, const int32_t *idx, const float *val, const float *s_doc,
+                bool check_ws, const void *ws, size_t ws_bytes, void *const *stage_events) {
+  // without the workspace check an aligned stand-in of unbounded size passes it
+  int rc = check_layer_route(b, true, QR, n_q, T, t_r, L_loc, h_q, k, s_doc,
+                             check_ws ? ws : reinterpret_cast<const void *>(256), check_ws ? ws_bytes : ~(size_t)0);
+  if (rc) return rc;
+  rc = check_layer_tail(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O, idx, val);
+  if (rc) return rc;
+  if (stage_events)
+    for (int i = 0; i < 4; ++i)
+      if (!stage_events[i]) return fail(MSA_ERR_ARG, "stage_events[%d] is null", i);
+  return MSA_OK;
+}
+
 int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,
                       int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0,
                       float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
                       size_t ws_bytes, void *const *stage_events, void *stream) {
   try {
-    int rc = check_layer_route(b, true, QR, n_q, T, t_r, L_loc, h_q, k, s_doc, ws, ws_bytes);
+    const int rc = check_layer(b, Q, K_loc, V_loc, QR, n_q, T, t_r, L_loc, h_q, k, pos0, scale, rope, O, idx, val,
+                               s_doc, true, ws, ws_bytes, stage_events);
     if (rc) return rc;
-    rc = check_layer_tail(b, Q, K_loc, V_loc, n_q, T, L_loc, h_q, k, pos0, scale, rope, O, idx, val);
+    return layer_forward_checked(b, Q, K_loc, V_loc, QR, n_q, T, t_r, L_loc, h_q, k, pos0, scale, rope, O, idx, val,
+                                 s_doc, ws, stage_events, stream);
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+int msa_layer_forward_noalloc(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,
+                              int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0,
+                              float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc,
+                              void *const *stage_events, void *stream) {
+  try {
+    // every argument and the size are checked before any device call: a layer
+    // whose workspace exceeds the static array is refused
+    int rc = check_layer(b, Q, K_loc, V_loc, QR, n_q, T, t_r, L_loc, h_q, k, pos0, scale, rope, O, idx, val, s_doc,
+                         false, nullptr, 0, stage_events);
     if (rc) return rc;
-    if (stage_events)
-      for (int i = 0; i < 4; ++i)
-        if (!stage_events[i]) return fail(MSA_ERR_ARG, "stage_events[%d] is null", i);
-    const LayerCtx c{b, n_q, T, t_r, L_loc, h_q, k, static_cast<char *>(ws), layer_ws(b, n_q, T, t_r, L_loc, h_q, k),
-                     (hipStream_t)stream, stage_events};
-    hipError_t e = layer_route(c, QR, s_doc);
-    if (e == hipSuccess) e = layer_tail(c, Q, K_loc, V_loc, pos0, scale, rope, O, idx, val, s_doc);
-    return e == hipSuccess ? ok() : dev_fail(e, "layer_forward");
+    const size_t need = layer_ws(b, n_q, T, t_r, L_loc, h_q, k).total;
+    if (need > (size_t)MSA_STATIC_WORKSPACE_BYTES)
+      return fail(MSA_ERR_WORKSPACE, "this layer needs a %zu-byte workspace; the static workspace holds %zu bytes",
+                  need, (size_t)MSA_STATIC_WORKSPACE_BYTES);
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    return layer_forward_checked(b, Q, K_loc, V_loc, QR, n_q, T, t_r, L_loc, h_q, k, pos0, scale, rope, O, idx, val,
+                                 s_doc, ws, stage_events, stream);
   } catch (...) {
     return fail(MSA_ERR_DEVICE, "internal error");
   }

@@ -251,3 +251,26 @@ def test_rope_tables_must_be_16_byte_aligned():
     b = _bank(doc_tok_off_host=tok.ctypes.data, doc_chunk_off_host=ch.ctypes.data)
     assert _code(msa.msa_pool_memory, b, A, A, A, 0, 1, _rope(max_pos=512, cos=MIS.addr), 0) == L.MSA_ERR_ARG
     assert "rope.cos" in msa.msa_last_error()
+
+
+def test_layer_noalloc_validation():
+    # the allocation-free layer validates like msa_layer_forward and refuses a
+    # layer whose workspace exceeds the static array, before any device call
+    b = _bank()
+    r = _rope()
+    args = [b, A, A, A, A, 1, 4, 4, 8, 32, 2, 2, 0.1, r, A, A, A, None]
+    bad = list(args)
+    bad[7] = 0                                              # t_r = 0
+    assert _code(msa.msa_layer_forward_noalloc, *bad, stream=0) == L.MSA_ERR_ARG
+    bad = list(args)
+    bad[4] = None                                           # QR
+    assert _code(msa.msa_layer_forward_noalloc, *bad, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_layer_forward_noalloc, *args, stage_events=[A.addr, 0, A.addr, A.addr],
+                 stream=0) == L.MSA_ERR_ARG
+    # 200,000 documents of 512 tokens and 64 single-token queries: far more than 16 MiB of workspace
+    lay = msa.msa_bank_layout([512] * 200_000, 128)
+    big = _bank(n_docs=200_000, n_chunks=lay["n_chunks"])
+    need = msa.msa_layer_workspace_bytes(big, 64, 1, 1, 1, 32, 16)
+    assert need > L.STATIC_WORKSPACE_BYTES
+    e = _code(msa.msa_layer_forward_noalloc, big, A, A, A, A, 64, 1, 1, 1, 32, 16, 16, 0.1, r, A, A, A, None, stream=0)
+    assert e == L.MSA_ERR_WORKSPACE and "static workspace" in msa.msa_last_error()
