@@ -288,6 +288,31 @@ int msa_layer_forward(const msa_bank *b, const void *Q, const void *K_loc, const
                       size_t ws_bytes, void *const *stage_events, void *stream);
 
 /*
+ * A Memory Interleave re-routing round ([HD] sparse strategy: routing
+ * alternates with generation and is redone after every round; [HD] practical
+ * advice: re-route after each iteration to use the updated context; [LH]
+ * Component 3): the layer of msa_layer_forward for a round whose router
+ * tokens are the previous round's plus t_new new ones, given the previous
+ * round's document scores.  The router score is a max over router tokens, so
+ *   s_doc[q][i] = max(s_doc_prev[q][i], max over the t_new new tokens' scores of document i)
+ * equals the score over all of the round's router tokens (the same value
+ * msa_layer_forward computes from all of them); only the new tokens are
+ * scanned.  Top-k and attention then run as in msa_layer_forward.
+ * QR_new: [n_q][t_new][h_r][d_r], the new router tokens only; s_doc_prev:
+ * [n_q][n_docs] fp32 input (the previous round's s_doc, e.g. from
+ * msa_layer_forward over the first round's tokens); s_doc: optional output of
+ * this round's scores, may be s_doc_prev itself (updated in place).  Other
+ * arguments as msa_layer_forward with t_r = t_new; workspace
+ * msa_layer_workspace_bytes(b, n_q, T, t_new, L_loc, h_q, k).  Errors: as
+ * msa_layer_forward, plus MSA_ERR_ARG for a null or misaligned s_doc_prev.
+ */
+int msa_layer_forward_reroute(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc,
+                              const void *QR_new, int32_t n_q, int32_t T, int32_t t_new, int32_t L_loc, int32_t h_q,
+                              int32_t k, int32_t pos0, float scale, const msa_rope *rope, const float *s_doc_prev,
+                              void *O, int32_t *idx, float *val, float *s_doc, void *ws, size_t ws_bytes,
+                              void *const *stage_events, void *stream);
+
+/*
  * msa_layer_forward for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same kernels and results, with the workspace taken from a static device

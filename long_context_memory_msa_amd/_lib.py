@@ -75,6 +75,8 @@ def _load():
         "msa_layer_workspace_bytes": ([bank_p, I32, I32, I32, I32, I32, I32], SZ),
         "msa_layer_forward": ([bank_p, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, rope_p, P, P, P, P, P, SZ,
                                P, P], ctypes.c_int),
+        "msa_layer_forward_reroute": ([bank_p, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, rope_p, P, P, P, P, P,
+                                       P, SZ, P, P], ctypes.c_int),
         "msa_layer_forward_noalloc": ([bank_p, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, rope_p, P, P, P, P,
                                        P, P], ctypes.c_int),
         "msa_scan_read_probe": ([bank_p, P, SZ, P], ctypes.c_int),
@@ -201,6 +203,18 @@ def msa_layer_forward(bank: MsaBank, Q, K_loc, V_loc, QR, n_q: int, T: int, t_r:
     _check(_lib.msa_layer_forward(ctypes.byref(bank), _ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(QR), n_q, T, t_r,
                                   L_loc, h_q, k, pos0, scale, ctypes.byref(rope), _ptr(O), _ptr(idx), _ptr(val),
                                   _ptr(s_doc), _ptr(ws), ws_bytes, ev, _stream(stream)))
+
+
+def msa_layer_forward_reroute(bank: MsaBank, Q, K_loc, V_loc, QR_new, n_q: int, T: int, t_new: int, L_loc: int,
+                              h_q: int, k: int, pos0: int, scale: float, rope: MsaRope, s_doc_prev, O, idx, val, s_doc,
+                              ws, ws_bytes: int, stage_events: Optional[Sequence[int]] = None, stream=None) -> None:
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * 4)(*stage_events)
+    _check(_lib.msa_layer_forward_reroute(ctypes.byref(bank), _ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(QR_new), n_q,
+                                          T, t_new, L_loc, h_q, k, pos0, scale, ctypes.byref(rope), _ptr(s_doc_prev),
+                                          _ptr(O), _ptr(idx), _ptr(val), _ptr(s_doc), _ptr(ws), ws_bytes, ev,
+                                          _stream(stream)))
 
 
 STATIC_WORKSPACE_BYTES = 16 << 20  # include/msa.h MSA_STATIC_WORKSPACE_BYTES

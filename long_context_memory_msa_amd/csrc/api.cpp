@@ -252,6 +252,12 @@ struct LayerCtx {
   LayerWs lw;
   hipStream_t s;
   void *const *ev;
+  // re-routing round: the document keys start from these scores (the previous
+  // round's), and the scan maxes the new router tokens into them
+  const float *prev = nullptr;
+  // single-writer scan (records, no atomics): one writer per (query, document)
+  // score and no previous scores to fold in
+  bool single() const { return !prev && msa::route_single_writer(t_r); }
   void *rt_ws() const { return w + lw.scores; }
   void *tk_ws() const { return w + lw.scores + lw.route; }
   void *at_ws() const { return w + lw.scores + lw.route + lw.topk; }
@@ -265,7 +271,7 @@ struct LayerCtx {
 // workspace; otherwise the document keys are zeroed and maxed atomically.
 hipError_t layer_route(const LayerCtx &c, const void *QR, float *s_doc) {
   hipError_t e = hipSuccess;
-  if (msa::route_single_writer(c.t_r)) {
+  if (c.single()) {
     msa::RouteArgs ra = route_args(c.b, QR, c.n_q, c.t_r, static_cast<float *>(c.rt_ws()), c.scores(s_doc), nullptr,
                                    nullptr);
     e = c.rec(0);
@@ -276,12 +282,14 @@ hipError_t layer_route(const LayerCtx &c, const void *QR, float *s_doc) {
     msa::RouteArgs ra = route_args(c.b, QR, c.n_q, c.t_r, nullptr, nullptr, keys, nullptr);
     ra.qinv = static_cast<float *>(c.rt_ws());
     if (msa::route_use_wide(c.b->dtype, c.b->h_r, c.b->d_r, c.t_r)) {
-      // the many-row scan's pre-kernel zeroes the keys
+      // the many-row scan's pre-kernel zeroes the keys (or sets them to the
+      // previous round's scores)
       ra.zero = keys;
       ra.n_zero = (int64_t)nd;
+      ra.init = c.prev;
       e = c.rec(0);
     } else {
-      e = msa::launch_fill_u32(keys, nd, 0u, c.s);
+      e = c.prev ? msa::launch_keys_from_scores(keys, c.prev, nd, c.s) : msa::launch_fill_u32(keys, nd, 0u, c.s);
       if (e == hipSuccess) e = c.rec(0);
     }
     if (e == hipSuccess) e = msa::launch_route_scan(ra, c.s);
@@ -296,7 +304,7 @@ hipError_t layer_tail(const LayerCtx &c, const void *Q, const void *K_loc, const
   const msa_bank *b = c.b;
   hipError_t e = hipSuccess;
   int n_fused = 0;  // > 0: the attention selects from this many candidates per query
-  if (msa::route_single_writer(c.t_r)) {
+  if (c.single()) {
     float *scores = c.scores(s_doc);
     msa::RouteArgs ra = route_args(b, nullptr, c.n_q, c.t_r, static_cast<float *>(c.rt_ws()), scores, nullptr,
                                    nullptr);
@@ -642,9 +650,9 @@ size_t msa_layer_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int3
 int layer_forward_checked(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, const void *QR,
                           int32_t n_q, int32_t T, int32_t t_r, int32_t L_loc, int32_t h_q, int32_t k, int32_t pos0,
                           float scale, const msa_rope *rope, void *O, int32_t *idx, float *val, float *s_doc, void *ws,
-                          void *const *stage_events, void *stream) {
+                          void *const *stage_events, void *stream, const float *s_doc_prev = nullptr) {
   const LayerCtx c{b, n_q, T, t_r, L_loc, h_q, k, static_cast<char *>(ws), layer_ws(b, n_q, T, t_r, L_loc, h_q, k),
-                   (hipStream_t)stream, stage_events};
+                   (hipStream_t)stream, stage_events, s_doc_prev};
   hipError_t e = layer_route(c, QR, s_doc);
   if (e == hipSuccess) e = layer_tail(c, Q, K_loc, V_loc, pos0, scale, rope, O, idx, val, s_doc);
   return e == hipSuccess ? ok() : dev_fail(e, "layer_forward");
@@ -702,6 +710,23 @@ int msa_layer_forward_noalloc(const msa_bank *b, const void *Q, const void *K_lo
     if (rc) return rc;
     return layer_forward_checked(b, Q, K_loc, V_loc, QR, n_q, T, t_r, L_loc, h_q, k, pos0, scale, rope, O, idx, val,
                                  s_doc, ws, stage_events, stream);
+  } catch (...) {
+    return fail(MSA_ERR_DEVICE, "internal error");
+  }
+}
+
+int msa_layer_forward_reroute(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc,
+                              const void *QR_new, int32_t n_q, int32_t T, int32_t t_new, int32_t L_loc, int32_t h_q,
+                              int32_t k, int32_t pos0, float scale, const msa_rope *rope, const float *s_doc_prev,
+                              void *O, int32_t *idx, float *val, float *s_doc, void *ws, size_t ws_bytes,
+                              void *const *stage_events, void *stream) {
+  try {
+    const int rc = check_layer(b, Q, K_loc, V_loc, QR_new, n_q, T, t_new, L_loc, h_q, k, pos0, scale, rope, O, idx, val,
+                               s_doc, true, ws, ws_bytes, stage_events);
+    if (rc) return rc;
+    CHECK_PTR(s_doc_prev, 4, "s_doc_prev");
+    return layer_forward_checked(b, Q, K_loc, V_loc, QR_new, n_q, T, t_new, L_loc, h_q, k, pos0, scale, rope, O, idx,
+                                 val, s_doc, ws, stage_events, stream, s_doc_prev);
   } catch (...) {
     return fail(MSA_ERR_DEVICE, "internal error");
   }

@@ -55,9 +55,12 @@ struct RouteArgs {
   // many-row (wide) scan: (1/h_r)/||Q^R|| per head and query row, [h_r][n_q * t_r] (workspace)
   float *qinv;
   // many-row scan: words its pre-kernel sets to zero before the scan (the
-  // document keys, in place of a separate fill launch); null = none
+  // document keys, in place of a separate fill launch); null = none.  With
+  // init set, they are set to score_key(init[i]) instead (a re-routing
+  // round starts from the previous round's document scores).
   uint32_t *zero = nullptr;
   int64_t n_zero = 0;
+  const float *init = nullptr;
   // streaming scan: at most this many workgroups per compute unit in the
   // persistent grid (0 = as many as stay resident)
   int max_wg_per_cu = 0;
@@ -74,6 +77,8 @@ hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s);
 // writes one record per 16-chunk tile to a.edges
 hipError_t launch_scan_read_probe(const RouteArgs &a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
+// p[i] = score_key(init[i]): order-preserving keys of fp32 scores
+hipError_t launch_keys_from_scores(uint32_t *p, const float *init, size_t n, hipStream_t s);
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s);
 hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s);  // in place
 

@@ -56,6 +56,11 @@ __global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+__global__ void keys_from_scores_kernel(uint32_t *p, const float *init, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = score_key(init[i]);
+}
+
 __global__ void keys_to_scores_kernel(uint32_t *p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = __float_as_uint(key_score(p[i]));
@@ -496,6 +501,13 @@ hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_keys_from_scores(uint32_t *p, const float *init, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t g = std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(keys_from_scores_kernel, dim3((unsigned)g), dim3(256), 0, s, p, init, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_keys_to_scores(uint32_t *p, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   size_t g = std::min<size_t>((n + 255) / 256, 8192);
@@ -542,7 +554,11 @@ hipError_t launch_resolve_docs(const RouteArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_route_scan(const RouteArgs &a, hipStream_t s) {
-  if (a.n_chunks == 0) return a.zero ? launch_fill_u32(a.zero, (size_t)a.n_zero, 0u, s) : hipSuccess;
+  if (a.n_chunks == 0) {
+    if (!a.zero) return hipSuccess;
+    return a.init ? launch_keys_from_scores(a.zero, a.init, (size_t)a.n_zero, s)
+                  : launch_fill_u32(a.zero, (size_t)a.n_zero, 0u, s);
+  }
   if (!a.edges && a.qinv && route_use_wide(a.dtype, a.h_r, a.d_r, a.t_r)) return launch_route_wide(a, s);
   if (a.dtype == 0) return a.d_r == 64 ? route_by_hr<float, 64>(a, s) : route_by_hr<float, 128>(a, s);
   if (a.d_r == 256) return route_by_hr<bf16_t, 256>(a, s);  // a router twice the head width

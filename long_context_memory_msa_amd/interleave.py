@@ -7,8 +7,15 @@ Round r of layer l routes with all active tokens of the layer's context
 (T0 + append * r), then attends the tokens that are new in this round (T0 in
 round 0, ``append`` afterwards) over the selected documents plus the whole
 causal local context.  Appending is the caller's: the context tensors hold the
-whole final context and each round uses a prefix of it.  This module is a
-host loop over msa_layer_forward; all computation runs in the kernels.
+whole final context and each round uses a prefix of it.
+
+The router score is a max over router tokens, so a later round's document
+scores are the max of the previous round's and the new tokens' own: round 0
+runs msa_layer_forward over its T0 tokens, later rounds
+msa_layer_forward_reroute over the ``append`` new ones with the layer's
+previous scores -- the same scores as routing all active tokens again, for a
+fraction of the scan.  This module is a host loop over those calls; all
+computation runs in the kernels.
 """
 from __future__ import annotations
 
@@ -43,9 +50,10 @@ def interleave(banks: Sequence[Bank], rope: Rope, layers: Sequence[Dict[str, tor
     scale = _lib.default_scale(d) if scale is None else scale
     dev = layers[0]["Q"].device
     td = TORCH_DTYPE[banks[0].dtype]
-    # one workspace for the largest round
-    nb = max(_lib.msa_layer_workspace_bytes(b.c, n_q, T0 if r == 0 else append, T0 + append * r, T0 + append * r,
-                                            h_q, k)
+    # one workspace for the largest round (rounds after the first route only
+    # their new tokens)
+    nb = max(_lib.msa_layer_workspace_bytes(b.c, n_q, T0 if r == 0 else append, T0 if r == 0 else append,
+                                            T0 + append * r, h_q, k)
              for b in banks for r in range(rounds))
     # the copies of strided slices and the output tensors are made on the
     # stream the layer calls run on, so that the allocator and the kernels see
@@ -61,19 +69,26 @@ def interleave(banks: Sequence[Bank], rope: Rope, layers: Sequence[Dict[str, tor
 def _rounds(banks, rope, layers, T0, append, rounds, k, pos0, h_q, scale, want_scores, stream, nb, n_q, d, dev, td):
     ws = workspace(nb, dev)
     out = []
+    prev = [None] * len(banks)  # each layer's document scores after the previous round
     for r in range(rounds):
         L_act = T0 + append * r
         T_new = T0 if r == 0 else append
         res_r = []
-        for bank, inp in zip(banks, layers):
+        for li, (bank, inp) in enumerate(zip(banks, layers)):
             O = torch.empty((n_q, T_new, h_q, d), dtype=td, device=dev)
             idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
             val = torch.empty((n_q, k), dtype=torch.float32, device=dev)
-            s_doc = torch.empty((n_q, bank.n_docs), dtype=torch.float32, device=dev) if want_scores else None
-            _lib.msa_layer_forward(bank.c, _contig(inp["Q"][:, L_act - T_new:L_act]),
-                                   _contig(inp["K_loc"][:, :L_act]), _contig(inp["V_loc"][:, :L_act]),
-                                   _contig(inp["QR"][:, :L_act]), n_q, T_new, L_act, L_act, h_q, k, pos0, scale,
-                                   rope.c, O, idx, val, s_doc, ws, nb, None, stream)
+            s_doc = torch.empty((n_q, bank.n_docs), dtype=torch.float32, device=dev)
+            Q = _contig(inp["Q"][:, L_act - T_new:L_act])
+            K_loc, V_loc = _contig(inp["K_loc"][:, :L_act]), _contig(inp["V_loc"][:, :L_act])
+            if r == 0:
+                _lib.msa_layer_forward(bank.c, Q, K_loc, V_loc, _contig(inp["QR"][:, :L_act]), n_q, T_new, L_act,
+                                       L_act, h_q, k, pos0, scale, rope.c, O, idx, val, s_doc, ws, nb, None, stream)
+            else:
+                _lib.msa_layer_forward_reroute(bank.c, Q, K_loc, V_loc, _contig(inp["QR"][:, L_act - T_new:L_act]),
+                                               n_q, T_new, T_new, L_act, h_q, k, pos0, scale, rope.c, prev[li], O,
+                                               idx, val, s_doc, ws, nb, None, stream)
+            prev[li] = s_doc
             res = {"O": O, "idx": idx, "val": val}
             if want_scores:
                 res["s_doc"] = s_doc

@@ -274,3 +274,22 @@ def test_layer_noalloc_validation():
     assert need > L.STATIC_WORKSPACE_BYTES
     e = _code(msa.msa_layer_forward_noalloc, big, A, A, A, A, 64, 1, 1, 1, 32, 16, 16, 0.1, r, A, A, A, None, stream=0)
     assert e == L.MSA_ERR_WORKSPACE and "static workspace" in msa.msa_last_error()
+
+
+def test_layer_reroute_validation():
+    # the re-routing layer checks what msa_layer_forward checks, plus its previous scores
+    b = _bank()
+    r = _rope()
+    big = 1 << 30
+    args = [b, A, A, A, A, 1, 4, 4, 8, 32, 2, 2, 0.1, r, A, A, A, A, None, A, big]
+    msa.msa_layer_forward_reroute  # exported
+    bad = list(args)
+    bad[14] = None                                          # s_doc_prev
+    assert _code(msa.msa_layer_forward_reroute, *bad, stream=0) == L.MSA_ERR_ARG
+    bad = list(args)
+    bad[14] = _Fake(0x10002)                                # s_doc_prev not 4-byte aligned
+    assert _code(msa.msa_layer_forward_reroute, *bad, stream=0) == L.MSA_ERR_ARG
+    bad = list(args)
+    bad[7] = 0                                              # t_new = 0
+    assert _code(msa.msa_layer_forward_reroute, *bad, stream=0) == L.MSA_ERR_ARG
+    assert _code(msa.msa_layer_forward_reroute, *args[:20], 16, stream=0) == L.MSA_ERR_WORKSPACE

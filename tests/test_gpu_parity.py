@@ -599,3 +599,71 @@ def test_interleave_small(device):
                              ob_banks[layer]["kbar"], ob_banks[layer]["vbar"], ob_banks[layer]["doc_chunk_off"], gi,
                              w.pos0, base=w.rope_base)
             assert_attention_close(host(g_["O"]), o_ref)
+
+
+# Memory Interleave re-routing: a round whose router tokens are the previous
+# round's T0 plus t_new new ones, routed from the previous scores and the new
+# tokens only (msa_layer_forward_reroute), against the oracle's routing over
+# all T0 + t_new tokens; many-row (wide) and few-row scans for the new tokens,
+# a bank sliced for the top-k, in place and not
+@pytest.mark.parametrize("name,T0,t_new,n_q", [("16k", 96, 32, 1), ("16k", 64, 5, 2), ("decode", 7, 1, 16),
+                                                ("sliced", 3, 16, 4), ("interleave", 512, 64, 1)])
+def test_layer_reroute_equals_routing_every_token(device, name, T0, t_new, n_q):
+    L_act = T0 + t_new
+    if name == "sliced":
+        g = np.random.default_rng(21)
+        lens = g.integers(8, 41, size=9_000).astype(np.int64)
+        w = _wl("decode-100m", 200_000, doc_lens=lens, chunk=64, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, k=16, pos0=16)
+    else:
+        wname, bt = SMALL[name]
+        w = _wl(wname, bt)
+    w = dataclasses.replace(w, n_q=n_q, T=t_new, L_loc=L_act, T_route=L_act, gold=np.zeros((n_q, 0), np.int64))
+    log(f"reroute {name}: docs={w.n_docs} chunks={w.n_chunks} n_q={n_q} T0={T0} t_new={t_new}")
+    qi, K, V, KR = host_inputs(w)
+    ob = oracle_bank(w, K, V, KR)
+    bank, rope = gpu_bank_pooled(w, K, V, KR, device, 1)
+    QR, Q, Kl, Vl = query_views(w, qi, device)          # QR over all L_act router tokens
+    # the previous round's document scores: the first T0 router tokens
+    prev = torch.empty((n_q, w.n_docs), dtype=torch.float32, device=device)
+    nb0 = L.msa_route_workspace_bytes(bank.c, n_q, T0)
+    L.msa_route_score(bank.c, QR[:, :T0].contiguous(), n_q, T0, prev, None, M.workspace(nb0, device), nb0)
+    # the new tokens' own scores (same scan arithmetic per token), for the exact fold
+    new = torch.empty_like(prev)
+    nb1 = L.msa_route_workspace_bytes(bank.c, n_q, t_new)
+    L.msa_route_score(bank.c, QR[:, T0:].contiguous(), n_q, t_new, new, None, M.workspace(nb1, device), nb1)
+    torch.cuda.synchronize()
+    outs = []
+    for in_place in (False, True):
+        O_ = torch.empty((n_q, t_new, w.h_q, w.d), dtype=M.TORCH_DTYPE[w.dtype], device=device)
+        idx = torch.empty((n_q, w.k), dtype=torch.int32, device=device)
+        val = torch.empty((n_q, w.k), dtype=torch.float32, device=device)
+        p = prev.clone()
+        s_doc = p if in_place else torch.empty_like(prev)
+        nb = L.msa_layer_workspace_bytes(bank.c, n_q, t_new, t_new, L_act, w.h_q, w.k)
+        L.msa_layer_forward_reroute(bank.c, Q, Kl, Vl, QR[:, T0:].contiguous(), n_q, t_new, t_new, L_act, w.h_q, w.k,
+                                    w.pos0, L.default_scale(w.d), rope.c, p, O_, idx, val, s_doc,
+                                    M.workspace(nb, device), nb)
+        torch.cuda.synchronize()
+        if not in_place:
+            assert torch.equal(p, prev)                  # the input scores are left as they were
+        outs.append((O_, idx, val, s_doc))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+    O_, idx, val, s_doc = outs[0]
+    assert torch.equal(s_doc, torch.maximum(prev, new))  # the fold, exactly
+    # against the oracle's routing over every router token of the round
+    S = O.chunk_scores(qi["QR"][:, :L_act], ob["krbar"])
+    sd_o = O.doc_scores(S, ob["doc_chunk_off"])
+    assert np.abs(host(s_doc) - sd_o).max() <= 2e-3
+    gi = idx.cpu().numpy()
+    check_topk_property(s_doc.cpu().numpy(), gi, val.cpu().numpy(), w.k)
+    topk_set_valid(gi, sd_o, w.k)
+    o_ref = O.attend(qi["Q"][:, L_act - t_new:L_act], qi["K_loc"][:, :L_act], qi["V_loc"][:, :L_act], ob["kbar"],
+                     ob["vbar"], ob["doc_chunk_off"], gi, w.pos0, base=w.rope_base)
+    assert_attention_close(host(O_), o_ref)
+    # where the whole round's routing takes the same scan for every token
+    # (many-row tiles both ways), the layer over all tokens is identical
+    if T0 % 16 == 0 and t_new % 16 == 0 and t_new >= 32:
+        full = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
+        for x, y in zip((O_, idx, val, s_doc), full):
+            assert torch.equal(x, y)
