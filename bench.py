@@ -15,7 +15,10 @@ Two timed regions of --steps steps each: sequential msa_layer_forward calls
 on one stream (per-stage events: layer latency, the scan's HBM roofline), then
 independent batches through the decode pipeline (two route streams whose
 scans overlap, the top-k and attention of earlier batches on a third); the
-pipelined rate is the throughput `value`.  Prints one JSON line.
+pipelined rate is the throughput `value`.  The same line carries the Memory
+Interleave workload (18 routed layers x 10M-token banks, 3 rounds; MFMA-bound)
+as the `interleave` record, and the fp64 oracle's rate on the host's cores as
+`cpu_baseline` (timed first, before the GPU is used).  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -26,6 +29,11 @@ import resource
 import statistics
 import sys
 import time
+
+# the oracle baseline runs one single-threaded process per core: no BLAS
+# thread pools of its own (set before NumPy is imported)
+for _v in ("OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = "1"
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -126,10 +134,26 @@ def run_pipelined(bank, rope, w, scale, dev, QR, Q, Kl, Vl, idx, O_, args) -> fl
     return wall
 
 
-def cpu_baseline(w, qi, n_docs: int) -> dict:
+_CPU_JOB = {}  # inputs of the oracle scan, inherited by the forked workers
+
+
+def _scan_block(bounds):
+    """Worker: the oracle's router scores of chunks [a, b) (fp64, single thread)."""
+    import oracle as O
+
+    a, b = bounds
+    return O.chunk_scores(_CPU_JOB["QR"], _CPU_JOB["krbar"][a:b])
+
+
+def cpu_baseline(w, qi, n_docs: int, workers: int) -> dict:
     """The fp64 oracle's layer forward on the first ``n_docs`` documents of the
     bank (pooled-shape synthetic values; the oracle's time does not depend on
-    them), on this host's cores."""
+    them) on this host's cores: the router scan (oracle.chunk_scores) over
+    contiguous chunk blocks in ``workers`` forked single-threaded processes,
+    then the document max, top-k and attention (oracle functions) here.  Runs
+    before this process touches the GPU (the workers are forked from it)."""
+    import multiprocessing
+
     import numpy as np
 
     import oracle as O
@@ -151,28 +175,45 @@ def cpu_baseline(w, qi, n_docs: int) -> dict:
     }
     QR = qi["QR"][:, w.L_loc - w.T_route:w.L_loc]
     Q = qi["Q"][:, w.L_loc - w.T:w.L_loc]
-    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    _CPU_JOB.update(QR=QR, krbar=bank["krbar"])
+    cuts = np.linspace(0, N, workers + 1).astype(np.int64)
+    blocks = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    pool = multiprocessing.get_context("fork").Pool(len(blocks))   # workers start before the timed region
+    pool.map(int, range(len(blocks)))                              # ... and are all up
+    r0s, r0c = resource.getrusage(resource.RUSAGE_SELF), resource.getrusage(resource.RUSAGE_CHILDREN)
     t0 = time.perf_counter()
-    O.layer_forward(QR, Q, qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], bank, w.k, w.pos0, base=w.rope_base)
+    S = np.concatenate(pool.map(_scan_block, blocks, chunksize=1), axis=1)
+    s_doc = O.doc_scores(S, bank["doc_chunk_off"])
+    sel = O.topk(s_doc, w.k)
+    O.attend(Q, qi["K_loc"][:, :w.L_loc], qi["V_loc"][:, :w.L_loc], bank["kbar"], bank["vbar"],
+             bank["doc_chunk_off"], sel["idx"], w.pos0, base=w.rope_base)
     dt = time.perf_counter() - t0
-    r1 = resource.getrusage(resource.RUSAGE_SELF)
-    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    pool.close()
+    pool.join()
+    r1s, r1c = resource.getrusage(resource.RUSAGE_SELF), resource.getrusage(resource.RUSAGE_CHILDREN)
+    _CPU_JOB.clear()
+    cpu = sum((getattr(r1, f) - getattr(r0, f)) for r0, r1 in ((r0s, r1s), (r0c, r1c))
+              for f in ("ru_utime", "ru_stime"))
     tokens = int(lens.sum())
     return {
         "value": tokens / dt,
         "unit": "tokens/s",
-        "cores": max(1, round(cpu / dt)),
+        "cores": len(blocks),
         "kind": "oracle",
-        "sample": (f"oracle layer_forward (route + document max + top-k + attention, fp64 NumPy) over the first "
-                   f"{n_docs} documents ({tokens} tokens, {N} chunks) of the same bank layout and query batch; "
-                   f"{dt:.1f} s wall, {cpu:.1f} s CPU; {len(os.sched_getaffinity(0))} host threads available"),
+        "sample": (f"oracle layer forward (fp64 NumPy) over the first {n_docs} documents ({tokens} tokens, {N} "
+                   f"chunks) of the same bank layout and query batch: router scan (oracle.chunk_scores) over "
+                   f"{len(blocks)} chunk blocks in as many forked single-threaded processes, then document max, "
+                   f"top-k and attention in one; {dt:.2f} s wall, {cpu:.1f} s CPU "
+                   f"({cpu / dt:.1f} cores busy on average); {len(os.sched_getaffinity(0))} host cores available"),
     }
 
 
-def bench_interleave(args) -> int:
+def interleave_measure(args, n_passes: int) -> dict:
     """18 routed layers x 10M-token banks, 3 rounds of route -> top-k -> attend
-    (prefill 512 tokens, then 64 appended per round): throughput and the MFMA
-    rooflines of the router scan and of attention."""
+    (prefill 512 tokens, then 64 appended per round), ``n_passes`` timed passes
+    over the 54 layer calls: throughput, per-call latency per round, and the
+    MFMA rooflines of the router scan and of attention from the stage events
+    (median pass)."""
     import numpy as np
     import torch
 
@@ -195,31 +236,41 @@ def bench_interleave(args) -> int:
         layers.append({k: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev).to(torch.bfloat16)
                        for k, v in qi.items()})
     calls = [(r, l) for r in range(w.rounds) for l in range(w.n_layers)]
-    shapes = {}
+    shapes = {}   # round -> (active tokens, new tokens: attended, and routed by the scan)
     for r in range(w.rounds):
         L_act = w.L_loc + w.append * r
         shapes[r] = (L_act, w.L_loc if r == 0 else w.append)
-    nb = max(L.msa_layer_workspace_bytes(banks[0].c, 1, T, La, La, w.h_q, w.k) for La, T in shapes.values())
+    nb = max(L.msa_layer_workspace_bytes(banks[0].c, 1, T, T, La, w.h_q, w.k) for La, T in shapes.values())
     ws = M.workspace(nb, dev)
     outs = {r: torch.empty((1, shapes[r][1], w.h_q, w.d), dtype=torch.bfloat16, device=dev) for r in shapes}
     idxs = {c: torch.empty((1, w.k), dtype=torch.int32, device=dev) for c in calls}
     val = torch.empty((1, w.k), dtype=torch.float32, device=dev)
+    sdoc = [torch.empty((1, w.n_docs), dtype=torch.float32, device=dev) for _ in range(w.n_layers)]
     scale = L.default_scale(w.d)
 
     def run(events=None):
+        # round 0 routes its 512 tokens; later rounds scan only the 64 new
+        # tokens and fold in the layer's previous document scores (the same
+        # scores as routing every active token again)
         for i, (r, l) in enumerate(calls):
             La, T = shapes[r]
             inp = layers[l]
-            L.msa_layer_forward(banks[l].c, inp["Q"][:, La - T:La], inp["K_loc"][:, :La], inp["V_loc"][:, :La],
-                                inp["QR"][:, :La], 1, T, La, La, w.h_q, w.k, w.pos0, scale, rope.c, outs[r],
-                                idxs[(r, l)], val, None, ws, nb, None if events is None else events[4 * i:4 * i + 4])
+            ev = None if events is None else events[4 * i:4 * i + 4]
+            if r == 0:
+                L.msa_layer_forward(banks[l].c, inp["Q"][:, La - T:La], inp["K_loc"][:, :La], inp["V_loc"][:, :La],
+                                    inp["QR"][:, :La], 1, T, La, La, w.h_q, w.k, w.pos0, scale, rope.c, outs[r],
+                                    idxs[(r, l)], val, sdoc[l], ws, nb, ev)
+            else:
+                L.msa_layer_forward_reroute(banks[l].c, inp["Q"][:, La - T:La], inp["K_loc"][:, :La],
+                                            inp["V_loc"][:, :La], inp["QR"][:, La - T:La], 1, T, T, La, w.h_q, w.k,
+                                            w.pos0, scale, rope.c, sdoc[l], outs[r], idxs[(r, l)], val, sdoc[l], ws,
+                                            nb, ev)
 
     for _ in range(max(1, args.warmup)):
         run()
     torch.cuda.synchronize()
-    # args.steps timed passes; the pass with the median wall time is reported
     passes = []
-    for _ in range(max(1, args.steps)):
+    for _ in range(max(1, n_passes)):
         ev = Events(4 * len(calls))
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -228,36 +279,58 @@ def bench_interleave(args) -> int:
         wall = time.perf_counter() - t0
         route = [ev.ms(ev.h[4 * i], ev.h[4 * i + 1]) for i in range(len(calls))]
         attend = [ev.ms(ev.h[4 * i + 2], ev.h[4 * i + 3]) for i in range(len(calls))]
-        passes.append((wall, route, attend))
+        layer = [ev.ms(ev.h[4 * i], ev.h[4 * i + 3]) for i in range(len(calls))]
+        passes.append((wall, route, attend, layer))
+        ev.close()
     passes.sort(key=lambda p: p[0])
-    wall, route, attend = passes[len(passes) // 2]
+    wall, route, attend, layer = passes[len(passes) // 2]
     off = w.doc_chunk_off
     route_flop = attn_flop = 0.0
     for (r, l) in calls:
         La, T = shapes[r]
-        route_flop += 2.0 * La * w.n_chunks * w.h_r * w.d_r
+        route_flop += 2.0 * T * w.n_chunks * w.h_r * w.d_r   # the router tokens this call scans
         sel = idxs[(r, l)].cpu().numpy()[0]
         n_mem = int(sum(off[d + 1] - off[d] for d in sel))
         visible = sum(n_mem + (La - T + t) + 1 for t in range(T))
         attn_flop += 4.0 * w.h_q * w.d * visible
     peak = 2.5e15
-    rec = {
-        "metric": "Memory Interleave: memory tokens routed/sec over 18 layers x 3 rounds (10M-token banks)",
+    per_round = {f"round{r}": {"router_tokens": shapes[r][0], "tokens_scanned": shapes[r][1],
+                               "tokens_attended": shapes[r][1],
+                               "layer_call_ms_p50": statistics.median(
+                                   layer[i] for i, c in enumerate(calls) if c[0] == r),
+                               "route_ms_p50": statistics.median(route[i] for i, c in enumerate(calls) if c[0] == r),
+                               "attend_ms_p50": statistics.median(
+                                   attend[i] for i, c in enumerate(calls) if c[0] == r)}
+                 for r in range(w.rounds)}
+    del banks, layers, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": "18 routed layers x 10M tokens, docs U[256,4096], chunk 128, prefill 512 + 2 x 64, k=8",
         "value": w.n_tok * len(calls) / wall,
-        "unit": "tokens/s",
-        "n_gpus": 1,
+        "unit": "memory tokens routed/s",
         "ms_per_interleave": wall * 1e3,
         "passes": len(passes),
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": "18 routed layers x 10M tokens, docs U[256,4096], chunk 128, prefill 512 + 2 x 64, k=8",
-                   "n_chunks_per_layer": w.n_chunks, "layer_calls": len(calls)},
+        "n_chunks_per_layer": w.n_chunks,
+        "layer_calls": len(calls),
+        "rounds": per_round,
         "route": {"ms_total": sum(route), "tflop": route_flop / 1e12,
-                  "mfma_frac": route_flop / (sum(route) * 1e-3) / peak, "peak_tflops": peak / 1e12},
+                  "mfma_frac": route_flop / (sum(route) * 1e-3) / peak, "peak_tflops": peak / 1e12,
+                  "round0_mfma_frac": sum(2.0 * shapes[0][1] * w.n_chunks * w.h_r * w.d_r for c in calls if c[0] == 0)
+                  / (sum(route[i] for i, c in enumerate(calls) if c[0] == 0) * 1e-3) / peak,
+                  "note": "rounds after the first scan only their 64 new router tokens and fold in the previous "
+                          "round's document scores; tflop counts the tokens scanned"},
         "attend": {"ms_total": sum(attend), "tflop": attn_flop / 1e12,
                    "mfma_frac": attn_flop / (sum(attend) * 1e-3) / peak, "peak_tflops": peak / 1e12},
     }
-    print(json.dumps(rec), flush=True)
+
+
+def bench_interleave(args) -> int:
+    """The interleave workload's own line (not the headline)."""
+    rec = interleave_measure(args, args.steps)
+    out = {"metric": "Memory Interleave: memory tokens routed/sec over 18 layers x 3 rounds (10M-token banks)",
+           "value": rec.pop("value"), "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": rec.pop("workload")}, **rec}
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -490,6 +563,8 @@ def main() -> int:
                          "3 Memory Interleave rounds (MFMA-bound prefill report); tiered: the decode layer with "
                          "Kbar/Vbar in host memory, decode pipeline; append: the last 10%% of the documents "
                          "appended to an encoded bank; project: the router projection GEMM")
+    ap.add_argument("--no-interleave", action="store_true",
+                    help="decode: leave out the Memory Interleave sub-record (18 layers x 10M tokens)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -501,6 +576,18 @@ def main() -> int:
         return 2
 
     import numpy as np
+
+    from synth import workloads as W
+
+    # the oracle baseline runs first: its workers are forked from this process,
+    # which must not have touched the GPU yet
+    cpu_rec = None
+    if args.workload == "decode100m" and args.cpu_docs != 0 and not args.copy_calibration:
+        w = W.make_workload("decode-100m", bank_tokens=args.bank_tokens)
+        workers = max(1, len(os.sched_getaffinity(0)))
+        print(f"[bench] timing the oracle on {workers} host cores ...", file=sys.stderr, flush=True)
+        cpu_rec = cpu_baseline(w, W.query_inputs(w), args.cpu_docs, workers)
+
     import torch
 
     if args.copy_calibration:
@@ -513,7 +600,7 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return 0
 
-    from synth import device as sdev, workloads as W
+    from synth import device as sdev
     from long_context_memory_msa_amd import _lib as L, memory as M, offline
 
     dev = torch.device("cuda:0")
@@ -648,9 +735,14 @@ def main() -> int:
         "pool": {"slabs": enc["slabs"], "GB/s": pool_gbs, "frac": pool_gbs / HBM_PEAK_GBS},
         "gold_recovered": gold_ok,
     }
-    if args.cpu_docs != 0:
-        print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, qi, args.cpu_docs)
+    if not args.no_interleave:
+        # the MFMA-bound workload beside the headline (its own banks; the
+        # decode bank is released first)
+        del bank, ws
+        torch.cuda.empty_cache()
+        rec["interleave"] = interleave_measure(args, 3)
+    if cpu_rec is not None:
+        rec["cpu_baseline"] = cpu_rec
     print(json.dumps(rec), flush=True)
     return 0
 
