@@ -245,9 +245,12 @@ size_t msa_attend_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int
  *   O[q][t][h] = softmax(scale * <R(pos0 + s_t) Q[q][t][h], keys>) . values
  * with every memory key visible and local key s visible when s <= s_t.
  * Q: [n_q][T][h_q][d]; K_loc, V_loc: [n_q][L_loc][h_kv][d] (before RoPE);
- * idx: [n_q][k] int32 document ids (each < n_docs); O: [n_q][T][h_q][d],
- * bank dtype.  Errors: MSA_ERR_ARG (T > L_loc, h_q % h_kv, rope too short
- * for pos0 + L_loc, ...), MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE.
+ * idx: [n_q][k] int32 document ids in [0, n_docs) (device memory the host
+ * does not read: a query whose ids include one outside that range gets NaN
+ * in every element of its output instead of an error code); O:
+ * [n_q][T][h_q][d], bank dtype.  Errors: MSA_ERR_ARG (T > L_loc, h_q % h_kv,
+ * rope too short for pos0 + L_loc, ...), MSA_ERR_UNSUPPORTED,
+ * MSA_ERR_WORKSPACE.
  */
 int msa_sparse_attend(const msa_bank *b, const void *Q, const void *K_loc, const void *V_loc, int32_t n_q, int32_t T,
                       int32_t L_loc, int32_t h_q, const int32_t *idx, int32_t k, int32_t pos0, float scale,

@@ -37,7 +37,7 @@ namespace {
 constexpr int SPLIT_MUL = 4;
 constexpr int MIN_TILES = 2;
 
-constexpr int KT = 32;          // keys per tile
+constexpr int KT0 = 32;         // keys per MFMA k-step of O^T = V^T P^T (a tile holds NK of them)
 constexpr int MAX_K = 256;      // selected documents per query
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -62,8 +62,9 @@ struct SplitOut {
   float *l;  // [rows][n_split]
 };
 
-template <typename T, int D, int WGW>
+template <typename T, int D, int WGW, int NK>
 __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_split, int n_rbg, SplitOut so) {
+  constexpr int KT = KT0 * NK;                        // keys per tile
   using F = Frag<T>;
   using FT = typename F::type;
   constexpr int EL = F::EL, KW = F::KW, KS = D / KW;  // k-steps over the head dim
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   __shared__ int64_t sCB[MAX_K];      // first chunk of each selected document
   __shared__ __align__(16) uint32_t sHist[256];  // in-kernel selection: radix histogram
   __shared__ uint64_t sSel[128];                 // and the compacted / ranked winners
+  __shared__ int sBadK;                          // a document id outside [0, n_docs)
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, G = lane >> 4;
@@ -161,12 +163,15 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       }
     }
     int carry = 0;
+    bool any_bad = false;
     for (int base = 0; base < a.k; base += 64) {
       const int r = base + lane;
       int cnt = 0;
       if (r < a.k) {
         int doc = a.cand ? sel_doc : a.idx[(int64_t)q * a.k + r];
-        doc = doc < 0 ? 0 : (doc >= a.n_docs ? a.n_docs - 1 : doc);
+        const bool bad_doc = doc < 0 || doc >= a.n_docs;  // the query's output becomes NaN
+        any_bad |= __ballot(bad_doc) != 0;
+        doc = bad_doc ? 0 : doc;
         const int64_t c0 = a.doc_chunk_off[doc];
         cnt = (int)(a.doc_chunk_off[doc + 1] - c0);
         sCB[r] = c0;
@@ -180,10 +185,14 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       if (r < a.k) sP[r] = carry + x - cnt;
       carry += __shfl(x, 63, 64);
     }
-    if (lane == 0) sP[a.k] = carry;
+    if (lane == 0) {
+      sP[a.k] = carry;
+      sBadK = any_bad ? 1 : 0;
+    }
   }
   __syncthreads();
-  const int n_mem = sP[a.k];
+  const bool bad = sBadK != 0;
+  const int n_mem = bad ? 0 : sP[a.k];
   const int n_keys = n_mem + a.L_loc;
 
   const int last_row = std::min(R, (rbg * WGW + WGW) * 16) - 1;
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   int kps = (n_keys + n_split - 1) / n_split;
   kps = (kps + KT - 1) / KT * KT;
   const int k_lo = split * kps;
-  const int k_hi = std::min(std::min(n_keys, k_lo + kps), n_mem + s_last + 1);  // causal trim
+  const int k_hi = bad ? k_lo : std::min(std::min(n_keys, k_lo + kps), n_mem + s_last + 1);  // causal trim
 
   const float c2 = a.scale * LOG2E;
   float m_run = -INFINITY, l_run = 0.f;
@@ -313,20 +322,20 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
     __syncthreads();
 
     if (rb * 16 < R) {
-      // ---- S^T = K Q^T for the 32 keys (two 16-key blocks) -----------------
-      f32x4 sc[2];
+      // ---- S^T = K Q^T for the tile's keys (16-key blocks) --------------------
+      f32x4 sc[2 * NK];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < 2 * NK; ++b) {
         sc[b] = zero4();
         const T *kr = sK + (16 * b + col) * KROW + G * EL;
 #pragma unroll
         for (int s = 0; s < KS; ++s) sc[b] = mfma16(load_frag<T>(kr + s * KW), qf[s], sc[b]);
       }
       // lane holds keys 16 b + 4 G + i of column `row`
-      float x[2][4];
+      float x[2 * NK][4];
       float mt = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2 * NK; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = kb + 16 * b + 4 * G + i;
@@ -338,10 +347,10 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_run == -INFINITY) ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
-      float p[2][4];
+      float p[2 * NK][4];
       float ps = 0.f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2 * NK; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           p[b][i] = (x[b][i] == -INFINITY) ? 0.f : exp2f(x[b][i] - m_new);
@@ -358,31 +367,35 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
         for (int mb = 0; mb < D / 16; ++mb) {
           const T *vr = sV + (16 * mb + col) * VROW;
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int b = 0; b < 2 * NK; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               acc_o[mb] = mfma16(Elem<T>::to_f32(vr[16 * b + 4 * G + i]), p[b][i], acc_o[mb]);
         }
       } else {
-        // k-slots 0..3 <-> keys 4G..4G+3, slots 4..7 <-> keys 16+4G..16+4G+3
-        uint32_t w[4];
-        w[0] = (uint32_t)f32_to_bf16(p[0][0]) | ((uint32_t)f32_to_bf16(p[0][1]) << 16);
-        w[1] = (uint32_t)f32_to_bf16(p[0][2]) | ((uint32_t)f32_to_bf16(p[0][3]) << 16);
-        w[2] = (uint32_t)f32_to_bf16(p[1][0]) | ((uint32_t)f32_to_bf16(p[1][1]) << 16);
-        w[3] = (uint32_t)f32_to_bf16(p[1][2]) | ((uint32_t)f32_to_bf16(p[1][3]) << 16);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
-        // V^T operand of lane (col, G): dims 16 mb + col, keys 4G..4G+3 and
-        // 16+4G..16+4G+3.  ds_read_b64_tr_b16 hands lane i of a 16-lane group
-        // element j of the 4 x 16 block that lanes 4j + i/4 address (8 bytes
-        // each), so lane a of the group addresses key 4G + a/4, dims
-        // 16 mb + 4 (a % 4) .. +3 of the row-major V tile.
-        const T *vb = sV + (4 * G + col / 4) * VROW + 4 * (col % 4);
+        // per 32-key k-step ks: k-slots 0..3 <-> keys 32 ks + 4G..+3, slots
+        // 4..7 <-> keys 32 ks + 16 + 4G..+3
 #pragma unroll
-        for (int mb = 0; mb < D / 16; ++mb) {
-          const v4i16 v0 = lds_read_tr16(vb + 16 * mb);
-          const v4i16 v1 = lds_read_tr16(vb + 16 * VROW + 16 * mb);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-          acc_o[mb] = mfma16(vf, pf, acc_o[mb]);
+        for (int ks = 0; ks < NK; ++ks) {
+          uint32_t w[4];
+          w[0] = (uint32_t)f32_to_bf16(p[2 * ks][0]) | ((uint32_t)f32_to_bf16(p[2 * ks][1]) << 16);
+          w[1] = (uint32_t)f32_to_bf16(p[2 * ks][2]) | ((uint32_t)f32_to_bf16(p[2 * ks][3]) << 16);
+          w[2] = (uint32_t)f32_to_bf16(p[2 * ks + 1][0]) | ((uint32_t)f32_to_bf16(p[2 * ks + 1][1]) << 16);
+          w[3] = (uint32_t)f32_to_bf16(p[2 * ks + 1][2]) | ((uint32_t)f32_to_bf16(p[2 * ks + 1][3]) << 16);
+          const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
+          // V^T operand of lane (col, G): dims 16 mb + col, keys 4G..4G+3 and
+          // 16+4G..16+4G+3 of the k-step.  ds_read_b64_tr_b16 hands lane i of a
+          // 16-lane group element j of the 4 x 16 block that lanes 4j + i/4
+          // address (8 bytes each), so lane a of the group addresses key
+          // 4G + a/4, dims 16 mb + 4 (a % 4) .. +3 of the row-major V tile.
+          const T *vb = sV + (32 * ks + 4 * G + col / 4) * VROW + 4 * (col % 4);
+#pragma unroll
+          for (int mb = 0; mb < D / 16; ++mb) {
+            const v4i16 v0 = lds_read_tr16(vb + 16 * mb);
+            const v4i16 v1 = lds_read_tr16(vb + 16 * VROW + 16 * mb);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+            acc_o[mb] = mfma16(vf, pf, acc_o[mb]);
+          }
         }
       }
     }
@@ -396,7 +409,7 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   if (!row_ok) return;
   const int64_t orow = ((int64_t)q * a.T + t) * a.h_q + h;
   if (n_split == 1) {
-    const float inv = 1.0f / l_tot;
+    const float inv = bad ? __builtin_nanf("") : 1.0f / l_tot;
     T *op = static_cast<T *>(a.O) + orow * D + 4 * G;
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       *reinterpret_cast<float4 *>(po + 16 * mb) = float4{acc_o[mb][0], acc_o[mb][1], acc_o[mb][2], acc_o[mb][3]};
     if (G == 0) {
       so.m[orow * n_split + split] = m_run;
-      so.l[orow * n_split + split] = l_tot;
+      so.l[orow * n_split + split] = bad ? __builtin_nanf("") : l_tot;
     }
   }
 }
@@ -440,9 +453,413 @@ __global__ void attend_combine_kernel(int64_t rows, int n_split, SplitOut so, vo
   static_cast<T *>(O)[r * D + dd] = Elem<T>::from_f32(acc / L);
 }
 
+// 16 bytes of a row as fp32 values (8 bf16 or 4 fp32 elements)
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4 &w, float (&x)[16 / sizeof(T)]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(ws[e] << 16);
+      x[2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(ws[e]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void load_row16(const T *p, float (&x)[16 / sizeof(T)]) {
+  unpack16<T>(*reinterpret_cast<const uint4 *>(p), x);
+}
+
+// fp32 values <-> an MFMA operand fragment (bf16: 8 values, rounded to nearest even)
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type to_frag(const float (&x)[Frag<T>::EL]) {
+  if constexpr (Frag<T>::EL == 1) {
+    return x[0];
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
+    return __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
+  }
+}
+template <typename T>
+__device__ __forceinline__ void from_frag(const typename Frag<T>::type &f, float (&x)[Frag<T>::EL]) {
+  if constexpr (Frag<T>::EL == 1) {
+    x[0] = f;
+  } else {
+    const uint4 w = __builtin_bit_cast(uint4, f);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(ws[j] << 16);
+      x[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+// ---- single-token queries (decode) -------------------------------------------
+// One workgroup of DW waves per (query, KV head); the g query heads of the KV
+// head are the token's rows.  The work is the gather of the selected
+// documents' pooled rows, so no key or value tile is staged in LDS and there
+// is no barrier per tile:
+//  * waves take 16-key blocks in turn; a block's scores S^T = K Q^T come from
+//    MFMAs whose A operand is loaded straight from the key rows (lane: key
+//    l % 16, 16 bytes per k-step), Q^T in registers (column = query head);
+//  * the running softmax is kept per column; the block's probabilities go to
+//    a small LDS slot of the wave, from which the value side reads them;
+//  * values are read in row layout (a key row spread over LPK lanes, 16 bytes
+//    each) and accumulated in fp32 on the vector units, O[h][dims] per lane;
+//  * loads for NB blocks are in flight before any of them is used;
+//  * the waves' (max, sum, O) are merged through LDS at the end: one kernel,
+//    no split partials.
+// Four waves of about 200 VGPRs, two 16-key blocks in flight per wave: the
+// workgroup fits on a compute unit beside two persistent router-scan
+// workgroups (128 VGPRs per wave), so a decode pipeline's attention runs
+// during the next steps' scans.  Measured at the 100M-token decode layer (16
+// queries, k = 16): pipelined step 285 us against 304 us for eight waves of
+// three blocks (which does not fit beside the scans) and 307 us for the
+// many-row kernel with split merge; alone, the attention stage 35 us against
+// 31 us for eight waves.
+constexpr int DW = 4;          // waves per workgroup
+constexpr int DPASS = 1024;    // keys listed per pass (chunk ids in LDS)
+constexpr int DNB = 2;         // 16-key blocks in flight per wave
+
+template <typename T, int D, int GQ>
+__global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
+  using F = Frag<T>;
+  using FT = typename F::type;
+  constexpr int EL = F::EL, KW = F::KW, KS = D / KW;  // MFMA k-steps over the head dim
+  constexpr int EPL = 16 / sizeof(T);   // value elements per lane (one 16-byte load)
+  constexpr int LPK = D / EPL;          // lanes per value row
+  constexpr int KPI = 64 / LPK;         // value rows per load instruction
+  constexpr int VPB = 16 / KPI;         // value loads per lane per block
+  constexpr int NT = 64 * DW;
+  constexpr int NB = sizeof(T) == 2 ? DNB : 1;  // blocks in flight (fp32 operands take 8x the registers)
+  static_assert(GQ <= 16 && KPI >= 1 && 16 % KPI == 0, "decode layout");
+
+  __shared__ int32_t sP[MAX_K + 1];          // prefix of the selected documents' chunk counts
+  __shared__ int64_t sCB[MAX_K];             // first chunk of each selected document
+  __shared__ int32_t sDoc[MAX_K];
+  __shared__ int64_t sList[DPASS];           // chunk of each memory key of the pass (-1 - s: local key s)
+  __shared__ float sPr[DW][16][GQ + 1];      // a wave's block probabilities [key][head]
+  __shared__ float sAl[DW][GQ];              // and its rescale factors per head
+  __shared__ float sM[DW][GQ], sL[DW][GQ];
+  __shared__ float sAcc[DW][GQ][D];
+  __shared__ __align__(16) uint32_t sHist[256];
+  __shared__ uint64_t sSel[128];
+  __shared__ int sBad;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kvh = blockIdx.x % a.h_kv;
+  const int q = blockIdx.x / a.h_kv;
+  const int col = lane & 15, G = lane >> 4;  // MFMA layout: key / head column, k-slot group
+  const int vr = lane / LPK, e0 = (lane % LPK) * EPL;  // value layout: key slot, dims
+  const int s_q = a.L_loc - 1;               // local index of the query token
+
+  // Q^T fragments (B operand): column col = query head kvh * GQ + col, dims
+  // [KW s + EL G, +EL), rotated at pos0 + s_q, rounded to the operand type
+  FT qf[KS];
+  {
+    const bool ok = col < GQ;
+    const T *qp = static_cast<const T *>(a.Q) + ((int64_t)q * a.h_q + kvh * GQ + (ok ? col : 0)) * D;
+    float x[KS][EL];
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      if constexpr (EL == 8) {
+        float v[8];
+        load_row16<T>(qp + st * KW + G * EL, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[st][e] = ok ? v[e] : 0.f;
+      } else {
+        x[st][0] = ok ? Elem<T>::to_f32(qp[st * KW + G * EL]) : 0.f;
+      }
+    }
+    const int64_t crow = (int64_t)(a.pos0 + s_q) * (D / 2);
+#pragma unroll
+    for (int st = 0; st < KS / 2; ++st)
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int i = st * KW + G * EL + e;  // < D/2; partner i + D/2 is k-step st + KS/2
+        const float c = a.cos[crow + i], sn = a.sin[crow + i];
+        const float lo = x[st][e], hi = x[st + KS / 2][e];
+        x[st][e] = lo * c - hi * sn;
+        x[st + KS / 2][e] = lo * sn + hi * c;
+      }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qf[st] = to_frag<T>(x[st]);
+  }
+
+  // selected documents: the layer's in-kernel selection, or idx
+  if (wave == 0) {
+    if (a.cand) {
+      constexpr int CI = ATTEND_MAX_CAND / 64;
+      const uint64_t *cq = a.cand + (int64_t)q * a.n_cand;
+      uint64_t v[CI];
+#pragma unroll
+      for (int j = 0; j < CI; ++j) v[j] = j * 64 + lane < a.n_cand ? cq[j * 64 + lane] : 0;
+      const uint64_t e = wave_topk_sorted_fast<CI>(v, (uint32_t)a.k, sHist, sSel);
+      if (lane < a.k) {
+        sDoc[lane] = (int)(0xFFFFFFFFu - (uint32_t)e);
+        if (a.idx_out && kvh == 0) {
+          a.idx_out[(int64_t)q * a.k + lane] = sDoc[lane];
+          a.val_out[(int64_t)q * a.k + lane] = key_score((uint32_t)(e >> 32));
+        }
+      }
+    } else {
+      for (int r = lane; r < a.k; r += 64) sDoc[r] = a.idx[(int64_t)q * a.k + r];
+    }
+    if (lane == 0) sBad = 0;
+  }
+  __syncthreads();
+  // chunk ranges of the selected documents (an id outside [0, n_docs) makes
+  // the query's output NaN)
+  for (int r = tid; r < a.k; r += NT) {
+    const int doc = sDoc[r];
+    if (doc < 0 || doc >= a.n_docs) {
+      sBad = 1;
+      sCB[r] = 0;
+      sP[r] = 0;
+    } else {
+      const int64_t c0 = a.doc_chunk_off[doc];
+      sCB[r] = c0;
+      sP[r] = (int)(a.doc_chunk_off[doc + 1] - c0);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive prefix of the counts, 4 ranks per lane (k <= 256)
+    int c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * lane + j;
+      c[j] = r < a.k ? sP[r] : 0;
+      sum += c[j];
+    }
+    int x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    int run = x - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * lane + j;
+      if (r < a.k) sP[r] = run;
+      run += c[j];
+    }
+    if (lane == 63) sP[a.k] = x;
+  }
+  __syncthreads();
+  const bool bad = sBad != 0;
+  const int n_mem = bad ? 0 : sP[a.k];
+  const int n_keys = bad ? 0 : n_mem + a.L_loc;  // the query token sees every local key
+
+  const T *kbar = static_cast<const T *>(a.kbar) + (int64_t)kvh * a.kv_stride * D;
+  const T *vbar = static_cast<const T *>(a.vbar) + (int64_t)kvh * a.kv_stride * D;
+  const float c2 = a.scale * LOG2E;
+  float m_run = -INFINITY, l_run = 0.f;  // column col's running max; this lane's share of its sum
+  float acc[GQ][EPL];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+
+  for (int pb = 0; pb < n_keys; pb += DPASS) {
+    const int np = min(DPASS, n_keys - pb);
+    // the pass's keys: memory key j -> its chunk (rank by binary search), local key s -> -1 - s
+    for (int jl = tid; jl < np; jl += NT) {
+      const int j = pb + jl;
+      int64_t ent;
+      if (j < n_mem) {
+        int lo_r = 0, hi_r = a.k - 1;  // rank r with sP[r] <= j < sP[r+1]
+        while (lo_r < hi_r) {
+          const int mid = (lo_r + hi_r + 1) >> 1;
+          if (sP[mid] <= j) lo_r = mid; else hi_r = mid - 1;
+        }
+        ent = sCB[lo_r] + (j - sP[lo_r]);
+      } else {
+        ent = -1 - (int64_t)(j - n_mem);
+      }
+      sList[jl] = ent;
+    }
+    __syncthreads();
+    const int n_blk = (np + 15) / 16;
+    // wave w takes blocks w, w + DW, ...; DNB of them per batch
+    for (int b0 = wave; b0 < n_blk; b0 += DW * NB) {
+      FT kf[NB][KS];
+      uint4 vw[NB][VPB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int kb = (b0 + nb * DW) * 16;
+        // key rows (A operand): key kb + col, k-step st: dims KW st + EL G
+        {
+          const int jl = kb + col;
+          const int64_t ent = jl < np ? sList[jl] : 0;
+          const T *kp;
+          if (ent >= 0) {
+            kp = kbar + ent * D;
+          } else {
+            const int s = (int)(-1 - ent);
+            kp = static_cast<const T *>(a.K_loc) + (((int64_t)q * a.L_loc + s) * a.h_kv + kvh) * D;
+          }
+#pragma unroll
+          for (int st = 0; st < KS; ++st) kf[nb][st] = load_frag<T>(kp + st * KW + G * EL);
+        }
+        // value rows: keys kb + vr + KPI u, dims e0
+#pragma unroll
+        for (int u = 0; u < VPB; ++u) {
+          const int jl = kb + vr + KPI * u;
+          const int64_t ent = jl < np ? sList[jl] : 0;
+          const T *vp = ent >= 0 ? vbar + ent * D
+                                 : static_cast<const T *>(a.V_loc) +
+                                       (((int64_t)q * a.L_loc + (-1 - ent)) * a.h_kv + kvh) * D;
+          vw[nb][u] = *reinterpret_cast<const uint4 *>(vp + e0);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int kb = (b0 + nb * DW) * 16;
+        if (b0 + nb * DW >= n_blk) break;  // wave-uniform
+        // local keys: RoPE at pos0 + s (partner dims are k-step st + KS/2 of this lane)
+        {
+          const int jl = kb + col;
+          const int64_t ent = jl < np ? sList[jl] : 0;
+          if (ent < 0) {
+            const int64_t crow = (a.pos0 + (-1 - ent)) * (int64_t)(D / 2);
+#pragma unroll
+            for (int st = 0; st < KS / 2; ++st) {
+              float lo[EL], hi[EL];
+              from_frag<T>(kf[nb][st], lo);
+              from_frag<T>(kf[nb][st + KS / 2], hi);
+#pragma unroll
+              for (int e = 0; e < EL; ++e) {
+                const int i = st * KW + G * EL + e;
+                const float c = a.cos[crow + i], sn = a.sin[crow + i];
+                const float x0 = lo[e], x1 = hi[e];
+                lo[e] = x0 * c - x1 * sn;
+                hi[e] = x0 * sn + x1 * c;
+              }
+              kf[nb][st] = to_frag<T>(lo);
+              kf[nb][st + KS / 2] = to_frag<T>(hi);
+            }
+          }
+        }
+        // S^T = K Q^T: lane holds keys kb + 4G + i of head column col
+        f32x4 sc = zero4();
+#pragma unroll
+        for (int st = 0; st < KS; ++st) sc = mfma16(kf[nb][st], qf[st], sc);
+        float x[4], mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = col < GQ && kb + 4 * G + i < np;
+          x[i] = vis ? sc[i] * c2 : -INFINITY;
+          mt = fmaxf(mt, x[i]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
+          ps += pr;
+          if (col < GQ) sPr[wave][4 * G + i][col] = pr;
+        }
+        if (col < GQ && G == 0) sAl[wave][col] = alpha;
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+        wave_sync();
+        // O[h][dims] += p[key][h] V[key][dims] for this lane's keys vr + KPI u
+        float al[GQ];
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) al[h] = sAl[wave][h];
+#pragma unroll
+        for (int h = 0; h < GQ; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
+#pragma unroll
+        for (int u = 0; u < VPB; ++u) {
+          float v[EPL];
+          unpack16<T>(vw[nb][u], v);
+          const int key = vr + KPI * u;
+#pragma unroll
+          for (int h = 0; h < GQ; ++h) {
+            const float pr = sPr[wave][key][h];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr, v[e], acc[h][e]);
+          }
+        }
+        wave_sync();  // the slot is read before the next block rewrites it
+      }
+    }
+    __syncthreads();  // sList is read before the next pass rewrites it
+  }
+
+  // the wave's totals: the sum over its lanes of each column, O over its key slots
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+  if (lane < GQ) {  // lanes 0..GQ-1: column = head, G = 0
+    sM[wave][lane] = m_run;
+    sL[wave][lane] = l_run;
+  }
+  if (lane < LPK) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sAcc[wave][h][e0 + e] = acc[h][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < GQ * D; i += NT) {
+    const int h = i / D, dd = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) M = fmaxf(M, sM[w][h]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) {
+      const float wt = sM[w][h] == -INFINITY ? 0.f : exp2f(sM[w][h] - M);
+      L += wt * sL[w][h];
+      o += wt * sAcc[w][h][dd];
+    }
+    const float out = bad ? __builtin_nanf("") : o / L;
+    static_cast<T *>(a.O)[((int64_t)q * a.h_q + kvh * GQ + h) * D + dd] = Elem<T>::from_f32(out);
+  }
+}
+
+bool decode_ok(const AttendArgs &a) {
+  const int g = a.h_q / a.h_kv;
+  return a.T == 1 && (g == 1 || g == 2 || g == 4 || g == 8) && a.k <= MAX_K;
+}
+
+template <typename T, int D>
+hipError_t launch_decode(const AttendArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.n_q * a.h_kv)), block(64 * DW);
+  switch (a.h_q / a.h_kv) {
+    case 1: hipLaunchKernelGGL((attend_decode_kernel<T, D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attend_decode_kernel<T, D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attend_decode_kernel<T, D, 4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attend_decode_kernel<T, D, 8>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 struct Plan {
   int wgw, n_rb, n_rbg, n_split;
 };
+
+// 32-key k-steps per gathered tile of the many-row kernel (64 keys: twice the
+// bytes in flight per round trip of the tile pipeline)
+constexpr int ATT_NK = 2;
 
 Plan plan(const AttendArgs &a) {
   Plan p;
@@ -453,7 +870,7 @@ Plan plan(const AttendArgs &a) {
   p.n_rbg = (p.n_rb + p.wgw - 1) / p.wgw;
   const int64_t base = (int64_t)a.n_q * a.h_kv * p.n_rbg;
   const int64_t est_keys = std::min<int64_t>((int64_t)a.k * std::max(1, a.max_doc_chunks), a.n_chunks) + a.L_loc;
-  const int64_t tiles = (est_keys + KT - 1) / KT;
+  const int64_t tiles = (est_keys + KT0 - 1) / KT0;
   // keys/values in host memory: the host link bounds the gather, and a
   // workgroup per (query, KV head, row group) keeps enough rows in flight
   // while leaving the GPU to a concurrent router scan
@@ -468,7 +885,8 @@ Plan plan(const AttendArgs &a) {
 template <typename T, int D, int WGW>
 hipError_t launch_kernel(const AttendArgs &a, const Plan &p, const SplitOut &so, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_q * a.h_kv * p.n_rbg * p.n_split;
-  hipLaunchKernelGGL((attend_kernel<T, D, WGW>), dim3((unsigned)grid), dim3(64 * WGW), 0, s, a, p.n_split, p.n_rbg, so);
+  hipLaunchKernelGGL((attend_kernel<T, D, WGW, ATT_NK>), dim3((unsigned)grid), dim3(64 * WGW), 0, s, a, p.n_split,
+                     p.n_rbg, so);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const int64_t rows = (int64_t)a.n_q * a.T * a.h_q;
@@ -485,9 +903,10 @@ hipError_t dispatch_wgw(const AttendArgs &a, const Plan &p, const SplitOut &so, 
 
 }  // namespace
 
-int attend_splits(const AttendArgs &a) { return plan(a).n_split; }
+int attend_splits(const AttendArgs &a) { return decode_ok(a) ? 1 : plan(a).n_split; }
 
 size_t attend_ws_bytes(const AttendArgs &a) {
+  if (decode_ok(a)) return 0;
   const Plan p = plan(a);
   if (p.n_split == 1) return 0;
   const size_t rows = (size_t)a.n_q * a.T * a.h_q;
@@ -495,6 +914,10 @@ size_t attend_ws_bytes(const AttendArgs &a) {
 }
 
 hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s) {
+  if (decode_ok(a)) {
+    if (a.dtype == 0) return a.d == 64 ? launch_decode<float, 64>(a, s) : launch_decode<float, 128>(a, s);
+    return a.d == 64 ? launch_decode<bf16_t, 64>(a, s) : launch_decode<bf16_t, 128>(a, s);
+  }
   const Plan p = plan(a);
   const size_t rows = (size_t)a.n_q * a.T * a.h_q;
   SplitOut so{nullptr, nullptr, nullptr};

@@ -143,4 +143,58 @@ __device__ uint64_t wave_topk_sorted(const uint64_t (&v)[ITEMS], uint32_t need, 
   return r;
 }
 
+// Bitonic sort of one 64-bit value per lane across the wave, descending
+// (lane 0 ends with the largest).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = __shfl_xor(x, j, 64);
+      // in a block with (lane & k) == 0 the lower lane keeps the larger value
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  return x;
+}
+
+// wave_topk_sorted, first trying a threshold: the need-th largest of the lane
+// maxima is at most the need-th largest composite overall, so every winner is
+// at least that large; when at most 64 composites reach it (the usual case
+// for top-k candidates spread over many lanes) one sort of those gives the
+// result, otherwise the radix selection runs.  Same contract and result as
+// wave_topk_sorted (lane r: rank-r composite, 0 past the selected ones).
+template <int ITEMS>
+__device__ uint64_t wave_topk_sorted_fast(const uint64_t (&v)[ITEMS], uint32_t need, uint32_t *hist, uint64_t *sel) {
+  const int lane = threadIdx.x & 63;
+  uint64_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) mx = v[j] > mx ? v[j] : mx;
+  const uint64_t sorted_max = wave_sort_desc(mx);
+  const uint64_t tau = __shfl(sorted_max, (int)need - 1, 64);  // 0 when fewer lanes hold a composite
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) cnt += v[j] != 0 && v[j] >= tau;
+  int x = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  const int total = __shfl(x, 63, 64);
+  if (total > 64) return wave_topk_sorted<ITEMS>(v, need, hist, sel);  // wave-uniform
+  sel[lane] = 0;
+  wave_sync();
+  int pos = x - cnt;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (v[j] != 0 && v[j] >= tau) sel[pos++] = v[j];
+  wave_sync();
+  const uint64_t mine = sel[lane];
+  wave_sync();  // sel is read before any later reuse
+  const uint64_t r = wave_sort_desc(mine);
+  return (uint32_t)lane < need ? r : 0;
+}
+
 }  // namespace msa

@@ -221,9 +221,11 @@ def test_topk_isolated(device, n_q, n_docs, k):
 
 
 # ---------------------------------------------------------------------------
-def _attend_case(w, device, idx_h, T=None, L_loc=None):
+def _attend_case(w, device, idx_h, T=None, L_loc=None, idx_dev=None):
+    """The oracle's attention over idx_h and the GPU's over idx_dev (default idx_h)."""
     T = T or w.T
     L_loc = L_loc or w.L_loc
+    idx_dev = idx_h if idx_dev is None else idx_dev
     qi, K, V, KR = host_inputs(w)
     ob = oracle_bank(w, K, V, KR)
     Qh = qi["Q"][:, L_loc - T:L_loc]
@@ -235,7 +237,7 @@ def _attend_case(w, device, idx_h, T=None, L_loc=None):
     nb = L.msa_attend_workspace_bytes(bank.c, w.n_q, T, L_loc, w.h_q, k)
     ws = M.workspace(nb, device)
     L.msa_sparse_attend(bank.c, dev(Qh, w.dtype, device), dev(Klh, w.dtype, device), dev(Vlh, w.dtype, device),
-                        w.n_q, T, L_loc, w.h_q, torch.from_numpy(idx_h.astype(np.int32)).to(device), k, w.pos0,
+                        w.n_q, T, L_loc, w.h_q, torch.from_numpy(idx_dev.astype(np.int32)).to(device), k, w.pos0,
                         L.default_scale(w.d), rope.c, out, ws, nb)
     torch.cuda.synchronize()
     return host(out), want
@@ -438,6 +440,21 @@ def test_layer_sliced_multi_unit_documents(device, n_q, t_r):
     w = _wl("decode-100m", 200_000, doc_lens=lens, chunk=16, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, n_q=n_q, k=16,
             pos0=16, T_route=t_r, L_loc=t_r, gold=np.zeros((n_q, 0), dtype=np.int64))
     assert w.n_docs > 8192 and w.n_chunks > 2 * w.n_docs
+    _check_sliced_layer(w, device)
+
+
+@pytest.mark.parametrize("t_r", [1, 4, 32])
+def test_layer_few_slices_selected_in_attention(device, t_r):
+    # 2,000 documents (four 512-document slices of the top-k pass) and k = 8:
+    # the layer runs top-k pass 1 alone and the attention workgroups make the
+    # final selection, after the single-writer scan (one router token), the
+    # atomic-key scan (4 tokens) and the many-row scan (32 tokens)
+    g = np.random.default_rng(30 + t_r)
+    lens = g.integers(8, 41, size=2_000).astype(np.int64)
+    n_q = 3
+    w = _wl("decode-100m", 200_000, doc_lens=lens, chunk=64, h_kv=2, d=64, h_r=2, d_r=128 if t_r == 32 else 64,
+            h_q=4, n_q=n_q, k=8, pos0=8, T_route=t_r, L_loc=t_r, gold=np.zeros((n_q, 0), dtype=np.int64))
+    assert 1536 < w.n_docs <= 2048
     _check_sliced_layer(w, device)
 
 
@@ -667,3 +684,44 @@ def test_layer_reroute_equals_routing_every_token(device, name, T0, t_new, n_q):
         full = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
         for x, y in zip((O_, idx, val, s_doc), full):
             assert torch.equal(x, y)
+
+
+# single-token queries (the decode attention kernel) over every GQA grouping it
+# takes (1, 2, 4, 8 query heads per KV head), fp32 and bf16, head dims 64 and
+# 128, short and long local contexts
+@pytest.mark.parametrize("name,h_kv,h_q,L_loc", [("tiny", 2, 2, 5), ("tiny", 2, 4, 1), ("tiny", 1, 8, 40),
+                                                 ("16k", 8, 8, 3), ("16k", 4, 16, 1), ("16k", 2, 16, 70),
+                                                 ("decode", 8, 32, 1), ("decode", 8, 64, 9)])
+def test_attend_single_token_heads(device, name, h_kv, h_q, L_loc):
+    wname, bt = SMALL[name]
+    w = _wl(wname, bt)
+    n_q = min(w.n_q, 3) if name != "decode" else w.n_q
+    w = dataclasses.replace(w, h_kv=h_kv, h_q=h_q, n_q=n_q, T=1, L_loc=L_loc, T_route=1,
+                            gold=np.zeros((n_q, 0), np.int64))
+    g = np.random.default_rng(h_q + L_loc)
+    idx_h = np.stack([g.choice(w.n_docs, size=w.k, replace=False) for _ in range(n_q)])
+    log(f"attend T=1 {name} h_kv={h_kv} h_q={h_q} L_loc={L_loc} n_q={n_q} k={w.k}")
+    got, want = _attend_case(w, device, idx_h, 1, L_loc)
+    assert_attention_close(got, want)
+
+
+# a document id outside [0, n_docs) in one query's idx: that query's output is
+# NaN throughout (the kernel's own check; the host cannot read idx), the other
+# queries' outputs are as with valid ids
+@pytest.mark.parametrize("name,T", [("decode", 1), ("16k", 8)])
+def test_attend_invalid_document_id_gives_nan(device, name, T):
+    wname, bt = SMALL[name]
+    w = _wl(wname, bt)
+    n_q = 3
+    w = dataclasses.replace(w, n_q=n_q, T=T, L_loc=max(T, 4), T_route=1, gold=np.zeros((n_q, 0), np.int64))
+    g = np.random.default_rng(5)
+    idx_h = np.stack([g.choice(w.n_docs, size=w.k, replace=False) for _ in range(n_q)])
+    log(f"attend invalid id {name} T={T}")
+    for bad in (w.n_docs, -1):
+        ib = idx_h.copy()
+        ib[1, w.k // 2] = bad
+        got, want = _attend_case(w, device, np.where(ib < 0, 0, np.minimum(ib, w.n_docs - 1)), T, w.L_loc,
+                                 idx_dev=ib)
+        assert np.isnan(got[1]).all()
+        for q in (0, 2):
+            assert_attention_close(got[q:q + 1], want[q:q + 1])

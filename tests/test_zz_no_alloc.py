@@ -48,12 +48,13 @@ def _same(got, want):
 
 
 def test_noalloc_layer_equals_layer_forward_call_after_call(device):
-    # first the many-row (atomic-key) scan of the 16K-token prefill layer, the
-    # largest workspace here; then smaller layers on the same array: the decode
-    # layer (single-writer scan, single-pass top-k), a bank of 9,000 documents
-    # (top-k pass 1 completes the scores, the attention makes the final
-    # selection), fewer queries on a smaller bank, and the first layer again
-    # (its keys must start from zero after the others' records)
+    # layers of every scan and top-k form on the same array, largest workspace
+    # first and each later one smaller: the many-row (atomic-key) scan of the
+    # 16K-token prefill layer, the decode layer (single-writer scan,
+    # single-pass top-k), a bank of 9,000 documents (top-k pass 1 completes
+    # the scores, the attention makes the final selection), fewer queries on
+    # a smaller bank; then the first again (its keys and records must not
+    # depend on what the others left)
     g = np.random.default_rng(11)
     lens = g.integers(8, 41, size=9_000).astype(np.int64)
     sliced = dataclasses.replace(W.make_workload("decode-100m", bank_tokens=200_000), doc_lens=lens, chunk=64, h_kv=2,
@@ -62,18 +63,22 @@ def test_noalloc_layer_equals_layer_forward_call_after_call(device):
     decode = W.make_workload("decode-100m", bank_tokens=700_000)
     small = dataclasses.replace(W.make_workload("decode-100m", bank_tokens=300_000), n_q=5,
                                 gold=np.zeros((5, 0), np.int64))
-    sizes = []
-    for i, w in enumerate((rows, decode, sliced, small, rows)):
-        nb = L.msa_layer_workspace_bytes(_bank_c(w), w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k)
-        sizes.append(nb)
-        log(f"noalloc call {i}: {w.name} docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q} t_r={w.T_route} ws={nb}")
+    def ws_of(w):
+        return L.msa_layer_workspace_bytes(_bank_c(w), w.n_q, w.T, w.T_route, w.L_loc, w.h_q, w.k)
+
+    # largest workspace first, each later call smaller, then the first one again
+    order = sorted((rows, decode, sliced, small), key=ws_of, reverse=True)
+    sizes = [ws_of(w) for w in order]
+    assert all(b < a for a, b in zip(sizes, sizes[1:])), sizes
+    for i, w in enumerate(order + [order[0]]):
+        log(f"noalloc call {i}: {w.name} docs={w.n_docs} chunks={w.n_chunks} n_q={w.n_q} t_r={w.T_route} "
+            f"ws={ws_of(w)}")
         bank, rope, w, QR, Q, Kl, Vl = _case(w, device)
         want = run_layer(bank, rope, w, QR, Q, Kl, Vl, device)
         got = _noalloc(bank, rope, w, QR, Q, Kl, Vl, device)
         _same(got, want)
         got2 = _noalloc(bank, rope, w, QR, Q, Kl, Vl, device, with_scores=False)   # no s_doc output
         _same(got2, want)
-    assert sizes[1] < sizes[0] and sizes[2] < sizes[1]
 
 
 def _bank_c(w):
