@@ -183,7 +183,7 @@ LayerWs layer_ws(const msa_bank *b, int32_t n_q, int32_t T, int32_t t_r, int32_t
   LayerWs w;
   w.scores = align_up((size_t)n_q * b->n_docs * sizeof(uint32_t));
   w.route = align_up(msa::route_ws_bytes(b->dtype, b->h_r, b->d_r, b->n_chunks, b->n_docs, n_q, t_r));
-  w.topk = align_up(msa::topk_ws_bytes(n_q, b->n_docs, k));
+  w.topk = align_up(msa::topk_layer_ws_bytes(n_q, b->n_docs, k));
   msa::AttendArgs a = attend_args(b, nullptr, nullptr, nullptr, n_q, T, L_loc, h_q, nullptr, k, 0, 1.f, nullptr, nullptr);
   w.attend = align_up(msa::attend_ws_bytes(a));
   w.total = w.scores + w.route + w.topk + w.attend;
@@ -320,11 +320,11 @@ hipError_t layer_tail(const LayerCtx &c, const void *Q, const void *K_loc, const
     src.edges = msa::edge_layout(ra);
     src.doc_chunk_off = b->doc_chunk_off;
     src.t_r = c.t_r;
-    n_fused = msa::topk_fused_candidates(b->n_docs, c.k);  // 0 for single-pass banks
-    if (msa::topk_single_pass(b->n_docs)) {
-      e = msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
-    } else if (n_fused > 0) {
+    n_fused = msa::topk_fused_candidates(b->n_docs, c.k);  // 0 for one-slice banks or large k
+    if (n_fused > 0) {
       e = msa::launch_topk_pass1_resolve(src, c.n_q, b->n_docs, c.k, c.tk_ws(), c.s);
+    } else if (msa::topk_single_pass(b->n_docs)) {
+      e = msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
     } else {
       src.mode = msa::TopkSrc::SCORES;
       e = msa::launch_resolve_docs(ra, c.s);
@@ -336,13 +336,13 @@ hipError_t layer_tail(const LayerCtx &c, const void *Q, const void *K_loc, const
     msa::TopkSrc src{};
     src.mode = msa::TopkSrc::KEYS;
     src.keys = keys;
-    e = msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
+    src.scores = s_doc;  // the top-k writes the document scores as it reads their keys
+    // small k over several slices: pass 1 here, the final selection in the
+    // attention workgroups; otherwise the whole top-k
+    n_fused = msa::topk_fused_candidates(b->n_docs, c.k);
+    e = n_fused > 0 ? msa::launch_topk_pass1_keys(src, c.n_q, b->n_docs, c.k, c.tk_ws(), c.s)
+                    : msa::launch_topk(src, c.n_q, b->n_docs, c.k, idx, val, c.tk_ws(), c.s);
     if (e == hipSuccess) e = c.rec(2);
-    const size_t nd = (size_t)c.n_q * b->n_docs;
-    if (e == hipSuccess && s_doc) {
-      e = hipMemcpyAsync(s_doc, keys, nd * sizeof(uint32_t), hipMemcpyDeviceToDevice, c.s);
-      if (e == hipSuccess) e = msa::launch_keys_to_scores(reinterpret_cast<uint32_t *>(s_doc), nd, c.s);
-    }
   }
   if (e == hipSuccess) {
     msa::AttendArgs aa = attend_args(b, Q, K_loc, V_loc, c.n_q, c.T, c.L_loc, c.h_q, idx, c.k, pos0, scale, rope, O);

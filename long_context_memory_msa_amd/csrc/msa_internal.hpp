@@ -122,11 +122,13 @@ __device__ __forceinline__ float edge_doc_score(const EdgeLayout &L, const int64
 
 // ---- top-k -----------------------------------------------------------------
 size_t topk_ws_bytes(int n_q, int n_docs, int k);
+size_t topk_layer_ws_bytes(int n_q, int n_docs, int k);  // the layer's top-k (pass 1 alone included)
 bool topk_single_pass(int n_docs);  // one workgroup per query, no workspace
 // Where the document scores [n_q][n_docs] come from
 struct TopkSrc {
   enum Mode { SCORES = 0, KEYS = 1, EDGES = 2 } mode;
-  float *scores;                 // SCORES: read; EDGES: written (the completed document scores)
+  float *scores;                 // SCORES: read; EDGES: written (the completed document scores);
+                                 // KEYS: written when not null (the keys as scores)
   const uint32_t *keys;          // KEYS: order-preserving keys
   EdgeLayout edges;              // EDGES: the single-writer scan's output
   const int64_t *doc_chunk_off;  // EDGES
@@ -136,12 +138,16 @@ hipError_t launch_topk(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *
                        hipStream_t s);
 // Whether the final selection can be left to the attention kernel after
 // pass 1 alone (the per-slice candidates, ws as for launch_topk): the number
-// of candidates per query, or 0 when this top-k does not take that form.
+// of candidates per query, or 0 when this top-k does not take that form
+// (small k over more than one 512-document slice, at most ATTEND_MAX_CAND
+// candidates).
 int topk_fused_candidates(int n_docs, int k);
 // Pass 1 straight from a single-writer scan's records (EDGES source): one
 // workgroup per (slice, 4 queries) completes the slice's document scores
 // into src.scores and selects each query's k (no separate resolve kernel).
 hipError_t launch_topk_pass1_resolve(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s);
+// Pass 1 alone over order-preserving keys (KEYS source; writes src.scores when set).
+hipError_t launch_topk_pass1_keys(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s);
 
 // ---- router projection -------------------------------------------------------
 // Y[rows][out] = X[rows][hidden] W[out][hidden]^T, bf16 in and out, fp32 accumulation;

@@ -194,6 +194,7 @@ __device__ __forceinline__ uint64_t load_composite(const TopkSrc &src, int q, in
   uint32_t key;
   if constexpr (MODE == TopkSrc::KEYS) {
     key = src.keys[at];
+    if (src.scores) src.scores[at] = key_score(key);  // the document scores for the caller, when asked
   } else if constexpr (MODE == TopkSrc::SCORES) {
     key = score_key(src.scores[at]);
   } else {
@@ -334,33 +335,20 @@ constexpr int WS_ITEMS = WS_SLICE / 64;
 constexpr int WS_MAX_K = 32;  // k up to this uses the wave pass (k <= slice / 16)
 
 // The wave's k largest of its slice's composites (v[j]: document j * 64 + lane,
-// 0 past the slice) written to out[0, k), padded with zeros.
+// 0 past the slice) written to out[0, k) in descending order, padded with
+// zeros (k <= WS_MAX_K).  sel: 128 composites of LDS scratch for the wave.
 __device__ __forceinline__ void wave_slice_select(const uint64_t (&v)[WS_ITEMS], int n, int k, uint32_t *hist,
-                                                  uint64_t *out, int lane) {
+                                                  uint64_t *sel, uint64_t *out, int lane) {
   const uint32_t kk = (uint32_t)std::min(k, n);
-  int shift;
-  uint64_t prefix;
-  select_wave<WS_ITEMS>(v, kk, hist, &shift, &prefix);
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < WS_ITEMS; ++j) cnt += (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift));
-  int x = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  int pos = x - cnt;
-#pragma unroll
-  for (int j = 0; j < WS_ITEMS; ++j)
-    if (v[j] != 0 && (v[j] >> shift) >= (prefix >> shift)) out[pos++] = v[j];
-  for (int j = (int)kk + lane; j < k; j += 64) out[j] = 0;
+  const uint64_t r = wave_topk_sorted_fast<WS_ITEMS>(v, kk, hist, sel);  // lane r: rank r, 0 past kk
+  if (lane < k) out[lane] = r;
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, int k, int n_slices,
                                                         uint64_t *cand) {
   __shared__ __align__(16) uint32_t hist[4][256];
+  __shared__ uint64_t sel[4][128];
   const int q = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slice = blockIdx.x * 4 + wave;
   if (slice >= n_slices) return;  // whole wave; no workgroup barrier below
@@ -372,7 +360,7 @@ __global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, 
     const int i = j * 64 + lane;  // coalesced
     v[j] = i < n ? load_composite<MODE>(src, q, n_docs, lo + i) : 0;
   }
-  wave_slice_select(v, n, k, hist[wave], cand + ((int64_t)q * n_slices + slice) * k, lane);
+  wave_slice_select(v, n, k, hist[wave], sel[wave], cand + ((int64_t)q * n_slices + slice) * k, lane);
 }
 
 // ---- pass 1 from the scan's records, RS_Q queries per workgroup -----------------
@@ -433,6 +421,7 @@ __global__ __launch_bounds__(64 * RS_Q) void topk_pass1_resolve(TopkSrc src, int
                                                                  int n_slices, uint64_t *cand) {
   __shared__ float sS[RS_Q][WS_SLICE + 1];
   __shared__ __align__(16) uint32_t hist[RS_Q][256];
+  __shared__ uint64_t sel[RS_Q][128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slice = blockIdx.x, q0 = blockIdx.y * RS_Q;
   const int lo = slice * WS_SLICE;
@@ -462,7 +451,7 @@ __global__ __launch_bounds__(64 * RS_Q) void topk_pass1_resolve(TopkSrc src, int
     const int i = j * 64 + lane;
     v[j] = i < n ? composite(score_key(sS[wave][i]), lo + i) : 0;
   }
-  wave_slice_select(v, n, k, hist[wave], cand + ((int64_t)(q0 + wave) * n_slices + slice) * k, lane);
+  wave_slice_select(v, n, k, hist[wave], sel[wave], cand + ((int64_t)(q0 + wave) * n_slices + slice) * k, lane);
 }
 
 // ---- pass 2 over register-resident candidates (up to 8 per thread) ----------
@@ -570,6 +559,13 @@ size_t topk_ws_bytes(int n_q, int n_docs, int k) {
   return (size_t)n_q * n_slices_for(n_docs, k) * k * sizeof(uint64_t);
 }
 
+size_t topk_layer_ws_bytes(int n_q, int n_docs, int k) {
+  // pass 1's candidates also where the layer runs pass 1 alone on a bank the
+  // single pass could take (the attention makes the final selection)
+  const size_t fused = topk_fused_candidates(n_docs, k) > 0 ? (size_t)n_q * n_slices_for(n_docs, k) * k * sizeof(uint64_t) : 0;
+  return std::max(topk_ws_bytes(n_q, n_docs, k), fused);
+}
+
 template <int MODE>
 hipError_t topk_launch(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *idx, float *val, void *ws,
                        hipStream_t s) {
@@ -597,13 +593,22 @@ hipError_t topk_launch(const TopkSrc &src, int n_q, int n_docs, int k, int32_t *
 
 // The layer leaves the final selection to the attention kernel where it can.
 int topk_fused_candidates(int n_docs, int k) {
-  if (topk_single_pass(n_docs) || slice_for(k) != WS_SLICE) return 0;
+  // one slice: the single pass is as short as pass 1 alone
+  if (n_docs <= WS_SLICE || slice_for(k) != WS_SLICE) return 0;
   const int64_t n = (int64_t)n_slices_for(n_docs, k) * k;
   return n <= ATTEND_MAX_CAND ? (int)n : 0;
 }
 
+hipError_t launch_topk_pass1_keys(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s) {
+  if (src.mode != TopkSrc::KEYS || slice_for(k) != WS_SLICE) return hipErrorInvalidValue;
+  const int ns = n_slices_for(n_docs, k);
+  hipLaunchKernelGGL(topk_pass1_wave<TopkSrc::KEYS>, dim3((ns + 3) / 4, n_q), dim3(256), 0, s, src, n_docs, k, ns,
+                     static_cast<uint64_t *>(ws));
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_pass1_resolve(const TopkSrc &src, int n_q, int n_docs, int k, void *ws, hipStream_t s) {
-  if (src.mode != TopkSrc::EDGES || slice_for(k) != WS_SLICE || topk_single_pass(n_docs)) return hipErrorInvalidValue;
+  if (src.mode != TopkSrc::EDGES || slice_for(k) != WS_SLICE) return hipErrorInvalidValue;
   const int ns = n_slices_for(n_docs, k);
   hipLaunchKernelGGL(topk_pass1_resolve, dim3(ns, (n_q + RS_Q - 1) / RS_Q), dim3(64 * RS_Q), 0, s, src, n_q, n_docs,
                      k, ns, static_cast<uint64_t *>(ws));
