@@ -154,6 +154,15 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   }
 }
 
+// 16 bytes of the raw token stream, read once: a non-temporal load (the
+// slab is far larger than the caches; keeping it out of them measured 74-75 %
+// of HBM peak against 68-69 % with ordinary loads, both with 16 tokens per
+// lane in flight)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const bf16_t *p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+}
+
 // bf16, one wave per 1 KB piece of a token row (512 elements): pieces
 // [0, PK) of K, [PK, 2 PK) of V, [2 PK, 2 PK + PR) of K^R.
 template <int D, int DR>
@@ -183,9 +192,9 @@ __global__ __launch_bounds__(1024) void pool_pieces_kernel(PoolArgs a) {
     const bool lo = ei < D / 2;
     const float *cp = a.cos + j0 * (D / 2) + ei % (D / 2);
     const float *sp = a.sin + j0 * (D / 2) + ei % (D / 2);
-#pragma unroll 4
+#pragma unroll 16
     for (int t = 0; t < n_tok; ++t) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(src + (int64_t)t * rowlen);
+      const uint4 raw = load_stream16(src + (int64_t)t * rowlen);
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
       const float4 c0 = *reinterpret_cast<const float4 *>(cp + t * (D / 2));
       const float4 c1 = *reinterpret_cast<const float4 *>(cp + t * (D / 2) + 4);
@@ -202,9 +211,9 @@ __global__ __launch_bounds__(1024) void pool_pieces_kernel(PoolArgs a) {
       }
     }
   } else {
-#pragma unroll 8
+#pragma unroll 16
     for (int t = 0; t < n_tok; ++t) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(src + (int64_t)t * rowlen);
+      const uint4 raw = load_stream16(src + (int64_t)t * rowlen);
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
