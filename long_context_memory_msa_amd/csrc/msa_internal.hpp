@@ -67,6 +67,8 @@ struct RouteArgs {
 };
 bool route_single_writer(int t_r);                    // (query, document) scores have one writer
 bool route_use_wide(int dtype, int h_r, int d_r, int t_r);     // GEMM-tiled scan for many rows per query
+bool route_use_rows(int dtype, int h_r, int d_r, int n_q, int t_r);  // of those, few rows: a streaming scan
+hipError_t launch_route_rows(const RouteArgs &a, hipStream_t s);
 size_t route_wide_ws_bytes(int n_q, int t_r, int h_r);
 size_t route_ws_bytes(int dtype, int h_r, int d_r, int64_t n_chunks, int n_docs, int n_q, int t_r);
 // single-writer workspace: the records (this many bytes, a multiple of 256), then the interior-document scores

@@ -274,15 +274,231 @@ __global__ __launch_bounds__(2 * NW, 2) void route_wide_kernel(RouteArgs a, int 
   }
 }
 
+// Inclusive max-scan within runs of equal document over the 16 columns of a
+// lane group (consecutive chunks); match[j]: column col - 2^j holds the same
+// document.  The last column of a run then holds the run's max.
+__device__ __forceinline__ float run_max16(float v, const bool (&match)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float nv = __shfl_up(v, 1 << j, 16);
+    if (match[j]) v = fmaxf(v, nv);
+  }
+  return v;
+}
+
+// ---- streaming scan for a few row blocks (17-64 router rows) ------------------
+// The tiled many-row scan walks each 128-chunk tile through 16 dependent
+// stage fills, which caps it near 55 us over a 10M-token bank whatever its
+// row count up to 128; with at most four 16-row blocks the scan is bound by
+// the bank's bytes (about 63 FLOP per byte at 64 rows), so it streams the bank
+// once like the decode scan: persistent waves, a two-head prefetch ring of
+// 16-chunk tiles, and every loaded key fragment multiplied by the RB row
+// blocks' query fragments (held in LDS for the whole scan).  Rows are whole
+// 16-row blocks of one query each (t_r % 16 == 0); the document scores are
+// maxed atomically into order-preserving keys (zeroed or initialised before).
+constexpr int RW_WAVES = 8;  // waves per workgroup (one workgroup per compute unit: the queries fill LDS)
+
+template <int HR, int RB>
+__global__ __launch_bounds__(64 * RW_WAVES, 1) void route_rows_kernel(RouteArgs a, int64_t n_tiles, int64_t n_waves) {
+  constexpr int DR = 128, KW = 32, EL = 8, KS = DR / KW, NF = HR * KS;
+  constexpr int PD = HR < 2 ? HR : 2;  // heads in flight
+  static_assert(HR % PD == 0, "ring depth divides the head count");
+  __shared__ bf16x8 qfrag[RB][NF][64];
+  __shared__ __align__(16) float qinv[RB][HR][16];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, G = lane >> 4;
+  const int n_rows = a.n_q * a.t_r;
+  const int nrb = (n_rows + 15) / 16;  // row blocks in use (<= RB)
+  const bf16_t *qr = static_cast<const bf16_t *>(a.qr);
+  const bf16_t *krbar = static_cast<const bf16_t *>(a.krbar);
+  const int64_t wave_id = (int64_t)blockIdx.x * RW_WAVES + wave;
+
+  auto lane_chunk = [&](int64_t tl) -> int64_t {
+    const int64_t cp = tl * 16 + col;
+    return cp < a.n_chunks ? cp : a.n_chunks - 1;
+  };
+  float ik_cur[HR], ik_nxt[HR];
+  int doc_cur = -1, doc_nxt = -1;
+  auto load_meta = [&](int64_t tl, float (&ik)[HR], int &doc) {
+    const int64_t cp = lane_chunk(tl);
+    const float *ip = a.kr_inv_norm + cp * HR;
+    if constexpr (HR % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < HR / 4; ++j) {
+        const float4 v = reinterpret_cast<const float4 *>(ip)[j];
+        ik[4 * j] = v.x; ik[4 * j + 1] = v.y; ik[4 * j + 2] = v.z; ik[4 * j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < HR; ++j) ik[j] = ip[j];
+    }
+    const int d = a.chunk_doc[cp];
+    doc = (tl * 16 + col < a.n_chunks) ? d : -1;
+  };
+  // the key stream starts before the query staging (a wave without tiles
+  // reads a clamped, valid chunk and never uses it)
+  const int64_t t0 = wave_id;
+  bf16x8 ring[PD][KS];
+  const bf16_t *kp_cur = krbar + lane_chunk(t0) * (HR * DR) + G * EL;
+  const bf16_t *kp_nxt = kp_cur;
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+#pragma unroll
+    for (int st = 0; st < KS; ++st) ring[p][st] = load_frag<bf16_t>(kp_cur + p * DR + st * KW);
+  load_meta(t0, ik_cur, doc_cur);
+
+  // query fragments of the row blocks in MFMA A-operand order, and their norms
+  for (int e = threadIdx.x; e < RB * NF * 64; e += 64 * RW_WAVES) {
+    const int r = e / (NF * 64), f = (e / 64) % NF, l = e % 64, h = f / KS, st = f % KS;
+    const int row = r * 16 + (l & 15);
+    bf16x8 v = bf16x8{};
+    if (row < n_rows) v = load_frag<bf16_t>(qr + ((int64_t)row * HR + h) * DR + st * KW + (l >> 4) * EL);
+    qfrag[r][f][l] = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < RB * HR * 16; e += 64 * RW_WAVES) {
+    const int r = e / (HR * 16), h = (e / 16) % HR, rr = e % 16;
+    float ss = 0.f;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x8 v = qfrag[r][h * KS + st][16 * g + rr];
+#pragma unroll
+        for (int j = 0; j < EL; ++j) {
+          const float x = (float)v[j];
+          ss += x * x;
+        }
+      }
+    qinv[r][h][rr] = ss > 0.f ? (1.0f / sqrtf(ss)) * (1.0f / HR) : 0.f;
+  }
+  __syncthreads();
+
+  for (int64_t tile = t0; tile < n_tiles; tile += n_waves) {
+    const int64_t tile_next = tile + n_waves;
+    const bool has_next = tile_next < n_tiles;
+    const int64_t tile_pf = has_next ? tile_next : tile;
+    // next tile's loads issued unconditionally (a last tile re-reads its own final heads)
+    kp_nxt = krbar + lane_chunk(tile_pf) * (HR * DR) + G * EL + (has_next ? 0 : (HR - PD) * DR);
+    load_meta(tile_pf, ik_nxt, doc_nxt);
+    int zoff;  // opaque zero: the query fragments are read from LDS inside the loop
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zoff));
+    f32x4 S[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) S[r] = zero4();
+#pragma unroll
+    for (int h = 0; h < HR; ++h) {
+      const int slot = h % PD;
+      const float ik = ik_cur[h];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (r >= nrb) break;  // wave-uniform
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int st = 0; st < KS; ++st) acc = mfma16(qfrag[r][h * KS + st + zoff][lane], ring[slot][st], acc);
+        const float4 iq = *reinterpret_cast<const float4 *>(&qinv[r][h][4 * G]);
+        S[r][0] += acc[0] * (iq.x * ik);
+        S[r][1] += acc[1] * (iq.y * ik);
+        S[r][2] += acc[2] * (iq.z * ik);
+        S[r][3] += acc[3] * (iq.w * ik);
+      }
+      if (h + PD < HR) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) ring[slot][st] = load_frag<bf16_t>(kp_cur + (h + PD) * DR + st * KW);
+      } else {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) ring[slot][st] = load_frag<bf16_t>(kp_nxt + (h + PD - HR) * DR + st * KW);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int doc = doc_cur;
+    const int64_t c = tile * 16 + col;
+    const bool cv = c < a.n_chunks;
+    kp_cur = kp_nxt;
+#pragma unroll
+    for (int j = 0; j < HR; ++j) ik_cur[j] = ik_nxt[j];
+    doc_cur = doc_nxt;
+    // epilogue: per query, the max over its rows of each chunk, then the
+    // max over each run of chunks of one document, one atomic per run
+    const int doc_right = __shfl_down(doc, 1, 16);
+    const bool tail = (col == 15) || (doc_right != doc);
+    bool match[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int doc_left = __shfl_up(doc, 1 << j, 16);
+      match[j] = col >= (1 << j) && doc_left == doc;
+    }
+    float v = -INFINITY;
+    int q_cur = -1;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      if (r >= nrb) break;  // wave-uniform
+      float m = fmaxf(fmaxf(S[r][0], S[r][1]), fmaxf(S[r][2], S[r][3]));
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      const int q = r * 16 / a.t_r;  // the block's query
+      if (q != q_cur && q_cur >= 0) {  // a new query: publish the previous one's chunk maxima
+        if (a.chunk_out && G == 0 && cv) atomicMax(a.chunk_out + (int64_t)q_cur * a.n_chunks + c, score_key(v));
+        const float w = run_max16(cv ? v : -INFINITY, match);
+        if (G == 0 && tail && doc >= 0) atomicMax(a.doc_keys + (int64_t)q_cur * a.n_docs + doc, score_key(w));
+        v = -INFINITY;
+      }
+      q_cur = q;
+      v = fmaxf(v, m);
+    }
+    if (a.chunk_out && G == 0 && cv) atomicMax(a.chunk_out + (int64_t)q_cur * a.n_chunks + c, score_key(v));
+    const float w = run_max16(cv ? v : -INFINITY, match);
+    if (G == 0 && tail && doc >= 0) atomicMax(a.doc_keys + (int64_t)q_cur * a.n_docs + doc, score_key(w));
+  }
+}
+
 }  // namespace
 
 bool route_use_wide(int dtype, int h_r, int d_r, int t_r) {
   return dtype == 1 && (h_r == 1 || h_r == 2 || h_r == 4 || h_r == 8) && t_r % 16 == 0 && t_r >= 32 && d_r == 128;
 }
 
+bool route_use_rows(int dtype, int h_r, int d_r, int n_q, int t_r) {
+  return route_use_wide(dtype, h_r, d_r, t_r) && (int64_t)n_q * t_r <= 64;
+}
+
+namespace {
+template <int HR>
+hipError_t route_rows_launch(const RouteArgs &a, hipStream_t s) {
+  const int64_t n_tiles = (a.n_chunks + 15) / 16;
+  // one workgroup per compute unit; as many waves as still need the same
+  // number of rounds of tiles (no small set of waves on a last, partial round)
+  const int64_t slots = (int64_t)device_cu_count() * RW_WAVES;
+  const int64_t rounds = (n_tiles + slots - 1) / slots;
+  const int64_t waves = (n_tiles + rounds - 1) / rounds;
+  const int64_t wgs = (waves + RW_WAVES - 1) / RW_WAVES;
+  hipLaunchKernelGGL((route_rows_kernel<HR, 4>), dim3((unsigned)wgs), dim3(64 * RW_WAVES), 0, s, a, n_tiles,
+                     wgs * RW_WAVES);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_rows(const RouteArgs &a, hipStream_t s) {
+  if (a.zero) {  // the document keys start at zero, or at the previous round's scores
+    const hipError_t e = a.init ? launch_keys_from_scores(a.zero, a.init, (size_t)a.n_zero, s)
+                                : launch_fill_u32(a.zero, (size_t)a.n_zero, 0u, s);
+    if (e != hipSuccess) return e;
+  }
+  switch (a.h_r) {
+    case 1: return route_rows_launch<1>(a, s);
+    case 2: return route_rows_launch<2>(a, s);
+    case 4: return route_rows_launch<4>(a, s);
+    case 8: return route_rows_launch<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 size_t route_wide_ws_bytes(int n_q, int t_r, int h_r) { return (size_t)n_q * t_r * h_r * sizeof(float); }
 
 hipError_t launch_route_wide(const RouteArgs &a, hipStream_t s) {
+  if (route_use_rows(a.dtype, a.h_r, a.d_r, a.n_q, a.t_r)) return launch_route_rows(a, s);
   const int n_rows = a.n_q * a.t_r;
   const int n_pairs = n_rows * a.h_r;
   const int64_t threads = (int64_t)n_pairs * (128 / 8);
