@@ -230,7 +230,9 @@ size_t msa_topk_workspace_bytes(int32_t n_q, int32_t n_docs, int32_t k);
 int msa_topk(const float *s_doc, int32_t n_q, int32_t n_docs, int32_t k, int32_t *idx, float *val, void *ws,
              size_t ws_bytes, void *stream);
 
-/* Workspace bytes msa_sparse_attend needs for these sizes (0 on invalid sizes). */
+/* Workspace bytes msa_sparse_attend needs for these sizes on the current
+ * device (0 on invalid sizes; the amount depends on the device's compute-unit
+ * count, by which the work of single-token queries is split). */
 size_t msa_attend_workspace_bytes(const msa_bank *b, int32_t n_q, int32_t T, int32_t L_loc, int32_t h_q, int32_t k);
 
 /*

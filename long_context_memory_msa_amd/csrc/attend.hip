@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   __shared__ int32_t sP[MAX_K + 1];   // prefix of selected documents' chunk counts
   __shared__ int64_t sCB[MAX_K];      // first chunk of each selected document
   __shared__ __align__(16) uint32_t sHist[256];  // in-kernel selection: radix histogram
-  __shared__ uint64_t sSel[128];                 // and the compacted / ranked winners
+  __shared__ __align__(16) uint64_t sSel[128];   // and the compacted / ranked winners
   __shared__ int sBadK;                          // a document id outside [0, n_docs)
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -150,12 +150,17 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
     // in-kernel selection: rank-r document of this query in lane r (k <= 64)
     int sel_doc = 0;
     if (a.cand) {
+      // lane l: candidates [CI l, CI l + CI), whole sorted per-slice lists
       constexpr int CI = ATTEND_MAX_CAND / 64;
       const uint64_t *cq = a.cand + (int64_t)q * a.n_cand;
       uint64_t v[CI];
 #pragma unroll
-      for (int j = 0; j < CI; ++j) v[j] = j * 64 + lane < a.n_cand ? cq[j * 64 + lane] : 0;
-      const uint64_t e = wave_topk_sorted<CI>(v, (uint32_t)a.k, sHist, sSel);
+      for (int j = 0; j < CI; ++j) {
+        const int i = lane * CI + j;
+        const uint64_t x = cq[i < a.n_cand ? i : a.n_cand - 1];
+        v[j] = i < a.n_cand ? x : 0;
+      }
+      const uint64_t e = wave_topk_sorted_fast<CI>(v, (uint32_t)a.k, sHist, sSel);
       sel_doc = (int)(0xFFFFFFFFu - (uint32_t)e);
       if (a.idx_out && kvh == 0 && split == 0 && rbg == 0 && lane < a.k) {
         a.idx_out[(int64_t)q * a.k + lane] = sel_doc;
@@ -501,34 +506,40 @@ __device__ __forceinline__ void from_frag(const typename Frag<T>::type &f, float
 }
 
 // ---- single-token queries (decode) -------------------------------------------
-// One workgroup of DW waves per (query, KV head); the g query heads of the KV
-// head are the token's rows.  The work is the gather of the selected
-// documents' pooled rows, so no key or value tile is staged in LDS and there
-// is no barrier per tile:
-//  * waves take 16-key blocks in turn; a block's scores S^T = K Q^T come from
-//    MFMAs whose A operand is loaded straight from the key rows (lane: key
-//    l % 16, 16 bytes per k-step), Q^T in registers (column = query head);
+// ns workgroups of DW waves per (query, KV head) (decode_splits: enough for
+// one workgroup per compute unit, since a workgroup's gather is bound by its
+// compute unit's memory throughput); the g query heads of the KV head are the
+// token's rows.  The work is the gather of the selected documents' pooled
+// rows, so no key or value tile is staged in LDS and there is no barrier per
+// tile:
+//  * the ns * DW waves of a (query, KV head) take 16-key blocks in turn; a
+//    block's scores S^T = K Q^T come from MFMAs whose A operand is loaded
+//    straight from the key rows (lane: key l % 16, 16 bytes per k-step), Q^T
+//    in registers (column = query head);
 //  * the running softmax is kept per column; the block's probabilities go to
 //    a small LDS slot of the wave, from which the value side reads them;
 //  * values are read in row layout (a key row spread over LPK lanes, 16 bytes
 //    each) and accumulated in fp32 on the vector units, O[h][dims] per lane;
 //  * loads for NB blocks are in flight before any of them is used;
-//  * the waves' (max, sum, O) are merged through LDS at the end: one kernel,
-//    no split partials.
+//  * the waves' (max, sum, O) are merged through LDS; with ns > 1 the
+//    workgroups' merged partials go to attend_combine_kernel.
 // Four waves of about 200 VGPRs, two 16-key blocks in flight per wave: the
 // workgroup fits on a compute unit beside two persistent router-scan
 // workgroups (128 VGPRs per wave), so a decode pipeline's attention runs
 // during the next steps' scans.  Measured at the 100M-token decode layer (16
-// queries, k = 16): pipelined step 285 us against 304 us for eight waves of
-// three blocks (which does not fit beside the scans) and 307 us for the
-// many-row kernel with split merge; alone, the attention stage 35 us against
-// 31 us for eight waves.
+// queries, k = 16, one workgroup per (query, KV head)): pipelined step 285 us
+// against 304 us for eight waves of three blocks (which does not fit beside
+// the scans) and 307 us for the many-row kernel with split merge.  Two
+// workgroups per (query, KV head) (256 on 256 compute units): the layer's
+// top-k + attention 48 -> 37 us.  Measured and not kept for the layer's call:
+// four blocks in flight (39 us), the next batch's loads issued before the
+// current one is computed (two batches of registers: 39-41 us).
 constexpr int DW = 4;          // waves per workgroup
 constexpr int DPASS = 1024;    // keys listed per pass (chunk ids in LDS)
 constexpr int DNB = 2;         // 16-key blocks in flight per wave
 
 template <typename T, int D, int GQ>
-__global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, int ns, SplitOut so) {
   using F = Frag<T>;
   using FT = typename F::type;
   constexpr int EL = F::EL, KW = F::KW, KS = D / KW;  // MFMA k-steps over the head dim
@@ -549,15 +560,34 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
   __shared__ float sM[DW][GQ], sL[DW][GQ];
   __shared__ float sAcc[DW][GQ][D];
   __shared__ __align__(16) uint32_t sHist[256];
-  __shared__ uint64_t sSel[128];
+  __shared__ __align__(16) uint64_t sSel[128];
   __shared__ int sBad;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kvh = blockIdx.x % a.h_kv;
-  const int q = blockIdx.x / a.h_kv;
+  // ns workgroups share each (query, KV head): split s takes the blocks of
+  // "waves" s DW .. s DW + DW - 1 out of VW
+  const int split = blockIdx.x % ns;
+  const int kvh = (blockIdx.x / ns) % a.h_kv;
+  const int q = blockIdx.x / ns / a.h_kv;
+  const int VW = DW * ns;
   const int col = lane & 15, G = lane >> 4;  // MFMA layout: key / head column, k-slot group
   const int vr = lane / LPK, e0 = (lane % LPK) * EPL;  // value layout: key slot, dims
   const int s_q = a.L_loc - 1;               // local index of the query token
+
+  // the layer's candidates are loaded first, so that their round trip
+  // overlaps that of the query rows.  Lane l takes candidates [CI l, CI l +
+  // CI): whole sorted per-slice lists, so that the lane maxima are list heads
+  // and the selection's threshold (the k-th largest head) passes few values.
+  constexpr int CI = ATTEND_MAX_CAND / 64;
+  uint64_t cv[CI];
+  if (a.cand && wave == 0) {
+    const uint64_t *cq = a.cand + (int64_t)q * a.n_cand;
+#pragma unroll
+    for (int j = 0; j < CI; ++j) {  // (unconditional loads: slots past n_cand re-read the last one,
+      const int i = lane * CI + j;    //  masked where the selection reads them)
+      cv[j] = cq[i < a.n_cand ? i : a.n_cand - 1];
+    }
+  }
 
   // Q^T fragments (B operand): column col = query head kvh * GQ + col, dims
   // [KW s + EL G, +EL), rotated at pos0 + s_q, rounded to the operand type
@@ -595,15 +625,12 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
   // selected documents: the layer's in-kernel selection, or idx
   if (wave == 0) {
     if (a.cand) {
-      constexpr int CI = ATTEND_MAX_CAND / 64;
-      const uint64_t *cq = a.cand + (int64_t)q * a.n_cand;
-      uint64_t v[CI];
 #pragma unroll
-      for (int j = 0; j < CI; ++j) v[j] = j * 64 + lane < a.n_cand ? cq[j * 64 + lane] : 0;
-      const uint64_t e = wave_topk_sorted_fast<CI>(v, (uint32_t)a.k, sHist, sSel);
+      for (int j = 0; j < CI; ++j) cv[j] = lane * CI + j < a.n_cand ? cv[j] : 0;
+      const uint64_t e = wave_topk_sorted_fast<CI>(cv, (uint32_t)a.k, sHist, sSel);
       if (lane < a.k) {
         sDoc[lane] = (int)(0xFFFFFFFFu - (uint32_t)e);
-        if (a.idx_out && kvh == 0) {
+        if (a.idx_out && kvh == 0 && split == 0) {
           a.idx_out[(int64_t)q * a.k + lane] = sDoc[lane];
           a.val_out[(int64_t)q * a.k + lane] = key_score((uint32_t)(e >> 32));
         }
@@ -670,30 +697,21 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
   for (int pb = 0; pb < n_keys; pb += DPASS) {
     const int np = min(DPASS, n_keys - pb);
     // the pass's keys: memory key j -> its chunk (rank by binary search), local key s -> -1 - s
-    for (int jl = tid; jl < np; jl += NT) {
-      const int j = pb + jl;
-      int64_t ent;
-      if (j < n_mem) {
-        int lo_r = 0, hi_r = a.k - 1;  // rank r with sP[r] <= j < sP[r+1]
-        while (lo_r < hi_r) {
-          const int mid = (lo_r + hi_r + 1) >> 1;
-          if (sP[mid] <= j) lo_r = mid; else hi_r = mid - 1;
-        }
-        ent = sCB[lo_r] + (j - sP[lo_r]);
-      } else {
-        ent = -1 - (int64_t)(j - n_mem);
-      }
-      sList[jl] = ent;
+    // 16 threads per rank write its chunks that fall in this pass (the
+    // local keys form rank k)
+    for (int r = tid >> 4; r <= a.k; r += NT >> 4) {
+      const int lo = r < a.k ? sP[r] : n_mem, hi = r < a.k ? sP[r + 1] : n_keys;
+      const int j1 = min(hi, pb + np);
+      for (int j = max(lo, pb) + (tid & 15); j < j1; j += 16)
+        sList[j - pb] = r < a.k ? sCB[r] + (j - lo) : -1 - (int64_t)(j - n_mem);
     }
     __syncthreads();
     const int n_blk = (np + 15) / 16;
-    // wave w takes blocks w, w + DW, ...; DNB of them per batch
-    for (int b0 = wave; b0 < n_blk; b0 += DW * NB) {
-      FT kf[NB][KS];
-      uint4 vw[NB][VPB];
+    // wave w of split s takes blocks s DW + w, + VW, ...; NB of them per batch
+    auto load_batch = [&](int b0, FT (&kf)[NB][KS], uint4 (&vw)[NB][VPB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int kb = (b0 + nb * DW) * 16;
+        const int kb = (b0 + nb * VW) * 16;
         // key rows (A operand): key kb + col, k-step st: dims KW st + EL G
         {
           const int jl = kb + col;
@@ -719,10 +737,12 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
           vw[nb][u] = *reinterpret_cast<const uint4 *>(vp + e0);
         }
       }
+    };
+    auto compute_batch = [&](int b0, FT (&kf)[NB][KS], uint4 (&vw)[NB][VPB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int kb = (b0 + nb * DW) * 16;
-        if (b0 + nb * DW >= n_blk) break;  // wave-uniform
+        const int kb = (b0 + nb * VW) * 16;
+        if (b0 + nb * VW >= n_blk) break;  // wave-uniform
         // local keys: RoPE at pos0 + s (partner dims are k-step st + KS/2 of this lane)
         {
           const int jl = kb + col;
@@ -795,6 +815,12 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
         }
         wave_sync();  // the slot is read before the next block rewrites it
       }
+    };
+    for (int b0 = split * DW + wave; b0 < n_blk; b0 += VW * NB) {
+      FT kf[NB][KS];
+      uint4 vw[NB][VPB];
+      load_batch(b0, kf, vw);
+      compute_batch(b0, kf, vw);
     }
     __syncthreads();  // sList is read before the next pass rewrites it
   }
@@ -831,8 +857,17 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a) {
       L += wt * sL[w][h];
       o += wt * sAcc[w][h][dd];
     }
-    const float out = bad ? __builtin_nanf("") : o / L;
-    static_cast<T *>(a.O)[((int64_t)q * a.h_q + kvh * GQ + h) * D + dd] = Elem<T>::from_f32(out);
+    const int64_t row = (int64_t)q * a.h_q + kvh * GQ + h;
+    if (ns == 1) {
+      const float out = bad ? __builtin_nanf("") : o / L;
+      static_cast<T *>(a.O)[row * D + dd] = Elem<T>::from_f32(out);
+    } else {  // partials for attend_combine_kernel (NaN sum: an id outside the bank)
+      so.o[(row * ns + split) * D + dd] = o;
+      if (dd == 0) {
+        so.m[row * ns + split] = M;
+        so.l[row * ns + split] = bad ? __builtin_nanf("") : L;
+      }
+    }
   }
 }
 
@@ -842,15 +877,36 @@ bool decode_ok(const AttendArgs &a) {
 }
 
 template <typename T, int D>
-hipError_t launch_decode(const AttendArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.n_q * a.h_kv)), block(64 * DW);
+hipError_t launch_decode(const AttendArgs &a, int ns, const SplitOut &so, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.n_q * a.h_kv * ns)), block(64 * DW);
   switch (a.h_q / a.h_kv) {
-    case 1: hipLaunchKernelGGL((attend_decode_kernel<T, D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attend_decode_kernel<T, D, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attend_decode_kernel<T, D, 4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attend_decode_kernel<T, D, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attend_decode_kernel<T, D, 1>), grid, block, 0, s, a, ns, so); break;
+    case 2: hipLaunchKernelGGL((attend_decode_kernel<T, D, 2>), grid, block, 0, s, a, ns, so); break;
+    case 4: hipLaunchKernelGGL((attend_decode_kernel<T, D, 4>), grid, block, 0, s, a, ns, so); break;
+    default: hipLaunchKernelGGL((attend_decode_kernel<T, D, 8>), grid, block, 0, s, a, ns, so); break;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  const int64_t rows = (int64_t)a.n_q * a.h_q;
+  const int64_t n = rows * D;
+  hipLaunchKernelGGL((attend_combine_kernel<T, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, rows, ns, so,
+                     a.O);
   return hipGetLastError();
+}
+
+// Workgroups per (query, KV head) of the decode kernel: enough to give every
+// compute unit one (a workgroup's gather is bound by its compute unit's
+// memory throughput), each split keeping at least two blocks per wave of the
+// estimated keys.  A function of the call's sizes only, so that the layer's
+// call and the call on its selection split alike.
+int decode_splits(const AttendArgs &a) {
+  if (a.kv_host) return 1;
+  const int64_t wgs = (int64_t)a.n_q * a.h_kv;
+  const int64_t est_keys = std::min<int64_t>((int64_t)a.k * std::max(1, a.max_doc_chunks), a.n_chunks) + a.L_loc;
+  const int64_t blocks = (est_keys + 15) / 16;
+  int64_t ns = device_cu_count() / std::max<int64_t>(1, wgs);
+  ns = std::min<int64_t>(ns, blocks / (2 * DW));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(ns, 4));
 }
 
 struct Plan {
@@ -903,30 +959,30 @@ hipError_t dispatch_wgw(const AttendArgs &a, const Plan &p, const SplitOut &so, 
 
 }  // namespace
 
-int attend_splits(const AttendArgs &a) { return decode_ok(a) ? 1 : plan(a).n_split; }
+int attend_splits(const AttendArgs &a) { return decode_ok(a) ? decode_splits(a) : plan(a).n_split; }
 
 size_t attend_ws_bytes(const AttendArgs &a) {
-  if (decode_ok(a)) return 0;
-  const Plan p = plan(a);
-  if (p.n_split == 1) return 0;
+  const int ns = attend_splits(a);
+  if (ns == 1) return 0;
   const size_t rows = (size_t)a.n_q * a.T * a.h_q;
-  return rows * p.n_split * (a.d + 2) * sizeof(float);
+  return rows * ns * (a.d + 2) * sizeof(float);
 }
 
 hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s) {
-  if (decode_ok(a)) {
-    if (a.dtype == 0) return a.d == 64 ? launch_decode<float, 64>(a, s) : launch_decode<float, 128>(a, s);
-    return a.d == 64 ? launch_decode<bf16_t, 64>(a, s) : launch_decode<bf16_t, 128>(a, s);
-  }
-  const Plan p = plan(a);
   const size_t rows = (size_t)a.n_q * a.T * a.h_q;
+  const int ns = attend_splits(a);
   SplitOut so{nullptr, nullptr, nullptr};
-  if (p.n_split > 1) {
+  if (ns > 1) {
     float *base = static_cast<float *>(ws);
     so.o = base;
-    so.m = base + rows * p.n_split * a.d;
-    so.l = so.m + rows * p.n_split;
+    so.m = base + rows * ns * a.d;
+    so.l = so.m + rows * ns;
   }
+  if (decode_ok(a)) {
+    if (a.dtype == 0) return a.d == 64 ? launch_decode<float, 64>(a, ns, so, s) : launch_decode<float, 128>(a, ns, so, s);
+    return a.d == 64 ? launch_decode<bf16_t, 64>(a, ns, so, s) : launch_decode<bf16_t, 128>(a, ns, so, s);
+  }
+  const Plan p = plan(a);
   if (a.dtype == 0) return a.d == 64 ? dispatch_wgw<float, 64>(a, p, so, s) : dispatch_wgw<float, 128>(a, p, so, s);
   return a.d == 64 ? dispatch_wgw<bf16_t, 64>(a, p, so, s) : dispatch_wgw<bf16_t, 128>(a, p, so, s);
 }

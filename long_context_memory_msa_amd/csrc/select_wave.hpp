@@ -143,58 +143,71 @@ __device__ uint64_t wave_topk_sorted(const uint64_t (&v)[ITEMS], uint32_t need, 
   return r;
 }
 
-// Bitonic sort of one 64-bit value per lane across the wave, descending
-// (lane 0 ends with the largest).
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
-  const int lane = threadIdx.x & 63;
+// Rank of this lane's value among the first n entries of an LDS array of
+// distinct 64-bit values (how many are larger).  Broadcast reads, 16 entries
+// per step with all eight 16-byte reads in flight before any compare.  arr
+// holds n rounded up to a multiple of 16 slots, those past n zero.
+__device__ __forceinline__ int lds_rank16(const uint64_t *arr, int n, uint64_t x) {
+  int r = 0;
+  for (int m = 0; m < n; m += 16) {  // (n is wave-uniform)
+    uint4 w[8];
 #pragma unroll
-  for (int k = 2; k <= 64; k <<= 1)
+    for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint4 *>(arr + m)[i];
 #pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t y = __shfl_xor(x, j, 64);
-      // in a block with (lane & k) == 0 the lower lane keeps the larger value
-      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-      x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
-    }
-  return x;
+    for (int i = 0; i < 8; ++i)
+      r += ((((uint64_t)w[i].y << 32) | w[i].x) > x) + ((((uint64_t)w[i].w << 32) | w[i].z) > x);
+  }
+  return r;
 }
 
 // wave_topk_sorted, first trying a threshold: the need-th largest of the lane
-// maxima is at most the need-th largest composite overall, so every winner is
-// at least that large; when at most 64 composites reach it (the usual case
-// for top-k candidates spread over many lanes) one sort of those gives the
-// result, otherwise the radix selection runs.  Same contract and result as
-// wave_topk_sorted (lane r: rank-r composite, 0 past the selected ones).
+// maxima's score keys is at most that of the need-th largest composite
+// overall, so every winner's key reaches it; when at most 64 composites do
+// (the usual case when each lane's composites are spread over the score
+// range, or are whole sorted lists) they are ranked among themselves,
+// otherwise the radix selection runs.  The threshold comes from a 32-step
+// binary search on ballot counts, the survivors are compacted by ballots and
+// ranked by counting larger survivors in LDS, so no step waits on a chain of
+// cross-lane shuffles.  Same contract and result as wave_topk_sorted (lane r:
+// rank-r composite, 0 past the selected ones; need <= 64; sel holds 128
+// slots, 16-byte aligned).
 template <int ITEMS>
 __device__ uint64_t wave_topk_sorted_fast(const uint64_t (&v)[ITEMS], uint32_t need, uint32_t *hist, uint64_t *sel) {
   const int lane = threadIdx.x & 63;
   uint64_t mx = 0;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) mx = v[j] > mx ? v[j] : mx;
-  const uint64_t sorted_max = wave_sort_desc(mx);
-  const uint64_t tau = __shfl(sorted_max, (int)need - 1, 64);  // 0 when fewer lanes hold a composite
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < ITEMS; ++j) cnt += v[j] != 0 && v[j] >= tau;
-  int x = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
+  const uint32_t key = (uint32_t)(mx >> 32);  // (an empty lane: 0)
+  // tau = the largest t with at least `need` lane keys >= t
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t t = tau | (1u << b);
+    if ((uint32_t)__popcll(__ballot(key >= t)) >= need) tau = t;
   }
-  const int total = __shfl(x, 63, 64);
-  if (total > 64) return wave_topk_sorted<ITEMS>(v, need, hist, sel);  // wave-uniform
-  sel[lane] = 0;
-  wave_sync();
-  int pos = x - cnt;
+  // survivors (key >= tau) compacted into sel[0, 64) in item-major order
+  int total = 0;
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j)
-    if (v[j] != 0 && v[j] >= tau) sel[pos++] = v[j];
+  for (int j = 0; j < ITEMS; ++j) {
+    const bool keep = v[j] != 0 && (uint32_t)(v[j] >> 32) >= tau;
+    const unsigned long long b = __ballot(keep);
+    const int pos = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+    if (keep && pos < 64) sel[pos] = v[j];
+    total += __popcll(b);
+  }
+  if (total > 64) {  // wave-uniform
+    wave_sync();
+    return wave_topk_sorted<ITEMS>(v, need, hist, sel);
+  }
+  if (lane >= total) sel[lane] = 0;  // lds_rank16 reads whole groups of 16
+  sel[64 + lane] = 0;
   wave_sync();
-  const uint64_t mine = sel[lane];
+  const uint64_t e = lane < total ? sel[lane] : 0;
+  const int r = lds_rank16(sel, total, e);
+  if (lane < total) sel[64 + r] = e;  // survivors are distinct: ranks are unique
+  wave_sync();
+  const uint64_t out = (uint32_t)lane < need ? sel[64 + lane] : 0;
   wave_sync();  // sel is read before any later reuse
-  const uint64_t r = wave_sort_desc(mine);
-  return (uint32_t)lane < need ? r : 0;
+  return out;
 }
 
 }  // namespace msa

@@ -348,7 +348,7 @@ template <int MODE>
 __global__ __launch_bounds__(256) void topk_pass1_wave(TopkSrc src, int n_docs, int k, int n_slices,
                                                         uint64_t *cand) {
   __shared__ __align__(16) uint32_t hist[4][256];
-  __shared__ uint64_t sel[4][128];
+  __shared__ __align__(16) uint64_t sel[4][128];
   const int q = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slice = blockIdx.x * 4 + wave;
   if (slice >= n_slices) return;  // whole wave; no workgroup barrier below
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64 * RS_Q) void topk_pass1_resolve(TopkSrc src, int
                                                                  int n_slices, uint64_t *cand) {
   __shared__ float sS[RS_Q][WS_SLICE + 1];
   __shared__ __align__(16) uint32_t hist[RS_Q][256];
-  __shared__ uint64_t sel[RS_Q][128];
+  __shared__ __align__(16) uint64_t sel[RS_Q][128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slice = blockIdx.x, q0 = blockIdx.y * RS_Q;
   const int lo = slice * WS_SLICE;
