@@ -150,15 +150,17 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
     // in-kernel selection: rank-r document of this query in lane r (k <= 64)
     int sel_doc = 0;
     if (a.cand) {
-      // lane l: candidates [CI l, CI l + CI), whole sorted per-slice lists
+      // lane l: candidates [c l, c l + c), runs of the sorted per-slice lists
       constexpr int CI = ATTEND_MAX_CAND / 64;
+      const int c = (a.n_cand + 63) / 64;
       const uint64_t *cq = a.cand + (int64_t)q * a.n_cand;
       uint64_t v[CI];
 #pragma unroll
       for (int j = 0; j < CI; ++j) {
-        const int i = lane * CI + j;
-        const uint64_t x = cq[i < a.n_cand ? i : a.n_cand - 1];
-        v[j] = i < a.n_cand ? x : 0;
+        const int i = lane * c + j;
+        const bool in = j < c && i < a.n_cand;
+        const uint64_t x = cq[in ? i : a.n_cand - 1];
+        v[j] = in ? x : 0;
       }
       const uint64_t e = wave_topk_sorted_fast<CI>(v, (uint32_t)a.k, sHist, sSel);
       sel_doc = (int)(0xFFFFFFFFu - (uint32_t)e);
@@ -225,6 +227,7 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   //   store: rotate local keys, convert, write K and V^T into LDS
   constexpr int UPT = (KT * NP + NT - 1) / NT;  // units per thread per tile (threads past the tile idle)
   uint4 rk[UPT][2], rv[UPT][2];
+  float rcs[UPT][EPS], rsn[UPT][EPS];  // rotation of a local key's unit, loaded with it
   int rpos[UPT];
   auto load_tile = [&](int kb) {
 #pragma unroll
@@ -260,6 +263,18 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
         rv[i][1] = *reinterpret_cast<const uint4 *>(vs + D / 2 + m * EPS);
       } else {
         rk[i][0] = rk[i][1] = rv[i][0] = rv[i][1] = uint4{0u, 0u, 0u, 0u};  // zeros: no NaN reaches P*V
+      }
+      // the rotation's cos/sin travel with the rows (a memory key's unit
+      // reads row 0 of the table and does not use it), not one round trip later
+      {
+        const int64_t crow = (int64_t)(rpos[i] >= 0 ? rpos[i] : 0) * (D / 2) + m * EPS;
+#pragma unroll
+        for (int e = 0; e < EPS; e += 4) {
+          const float4 cv4 = *reinterpret_cast<const float4 *>(a.cos + crow + e);
+          const float4 sv4 = *reinterpret_cast<const float4 *>(a.sin + crow + e);
+          rcs[i][e] = cv4.x; rcs[i][e + 1] = cv4.y; rcs[i][e + 2] = cv4.z; rcs[i][e + 3] = cv4.w;
+          rsn[i][e] = sv4.x; rsn[i][e + 1] = sv4.y; rsn[i][e + 2] = sv4.z; rsn[i][e + 3] = sv4.w;
+        }
       }
     }
   };
@@ -298,10 +313,9 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
         }
       }
       if (rpos[i] >= 0) {
-        const int64_t crow = (int64_t)rpos[i] * (D / 2) + m * EPS;
 #pragma unroll
         for (int e = 0; e < EPS; ++e) {
-          const float c = a.cos[crow + e], sn = a.sin[crow + e];
+          const float c = rcs[i][e], sn = rsn[i][e];
           const float x0 = lo[e], x1 = hi[e];
           lo[e] = x0 * c - x1 * sn;
           hi[e] = x0 * sn + x1 * c;
@@ -575,17 +589,20 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
   const int s_q = a.L_loc - 1;               // local index of the query token
 
   // the layer's candidates are loaded first, so that their round trip
-  // overlaps that of the query rows.  Lane l takes candidates [CI l, CI l +
-  // CI): whole sorted per-slice lists, so that the lane maxima are list heads
-  // and the selection's threshold (the k-th largest head) passes few values.
+  // overlaps that of the query rows.  Lane l takes candidates [c l, c l + c),
+  // c = ceil(n_cand / 64): runs of the sorted per-slice lists, so that the
+  // lane maxima are run heads and the selection's threshold (the k-th
+  // largest head) passes few values (dealt round-robin, a lane would hold
+  // the same rank of many lists).
   constexpr int CI = ATTEND_MAX_CAND / 64;
+  const int c_run = (a.n_cand + 63) / 64;
   uint64_t cv[CI];
   if (a.cand && wave == 0) {
     const uint64_t *cq = a.cand + (int64_t)q * a.n_cand;
 #pragma unroll
-    for (int j = 0; j < CI; ++j) {  // (unconditional loads: slots past n_cand re-read the last one,
-      const int i = lane * CI + j;    //  masked where the selection reads them)
-      cv[j] = cq[i < a.n_cand ? i : a.n_cand - 1];
+    for (int j = 0; j < CI; ++j) {  // (unconditional loads: slots past the run re-read the last one,
+      const int i = lane * c_run + j;  //  masked where the selection reads them)
+      cv[j] = cq[j < c_run && i < a.n_cand ? i : a.n_cand - 1];
     }
   }
 
@@ -626,7 +643,7 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
   if (wave == 0) {
     if (a.cand) {
 #pragma unroll
-      for (int j = 0; j < CI; ++j) cv[j] = lane * CI + j < a.n_cand ? cv[j] : 0;
+      for (int j = 0; j < CI; ++j) cv[j] = j < c_run && lane * c_run + j < a.n_cand ? cv[j] : 0;
       const uint64_t e = wave_topk_sorted_fast<CI>(cv, (uint32_t)a.k, sHist, sSel);
       if (lane < a.k) {
         sDoc[lane] = (int)(0xFFFFFFFFu - (uint32_t)e);
