@@ -62,8 +62,8 @@ struct SplitOut {
   float *l;  // [rows][n_split]
 };
 
-template <typename T, int D, int WGW, int NK>
-__global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_split, int n_rbg, SplitOut so) {
+template <typename T, int D, int WGW, int NK, int KH>
+__global__ __launch_bounds__(64 * WGW * KH) void attend_kernel(AttendArgs a, int n_split, int n_rbg, SplitOut so) {
   constexpr int KT = KT0 * NK;                        // keys per tile
   using F = Frag<T>;
   using FT = typename F::type;
@@ -73,7 +73,9 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   constexpr int KROW = D + VPack<T>::PAD;             // LDS row pitch of K (elements)
   constexpr bool VTR = sizeof(T) == 2;                // bf16: V row-major, transposed on read
   constexpr int VROW = VTR ? KROW : KT + VPack<T>::PAD;  // pitch of V rows (bf16) / of V^T rows (fp32)
-  constexpr int NT = 64 * WGW;
+  constexpr int NT = 64 * WGW * KH;
+  constexpr int BPW = 2 * NK / KH, KSW = NK / KH;    // 16-key blocks and 32-key k-steps per wave and tile
+  static_assert(KH == 1 || KH == 2, "one or two key halves");
 
   __shared__ __align__(16) T sK[KT * KROW];
   __shared__ __align__(16) T sV[VTR ? KT * VROW : D * VROW];
@@ -82,8 +84,11 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
   __shared__ __align__(16) uint32_t sHist[256];  // in-kernel selection: radix histogram
   __shared__ __align__(16) uint64_t sSel[128];   // and the compacted / ranked winners
   __shared__ int sBadK;                          // a document id outside [0, n_docs)
+  __shared__ float sMerge[KH > 1 ? WGW * 64 * (D / 4 + 2) : 1];  // second key half's (max, sum, O) per lane
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = (threadIdx.x >> 6) % WGW;  // row block of the group
+  const int kh = (threadIdx.x >> 6) / WGW;    // key half of each tile this wave takes (KH = 2)
   const int col = lane & 15, G = lane >> 4;
   int bid = blockIdx.x;
   const int split = bid % n_split; bid /= n_split;
@@ -342,38 +347,40 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
 
     if (rb * 16 < R) {
       // ---- S^T = K Q^T for the tile's keys (16-key blocks) --------------------
-      f32x4 sc[2 * NK];
+      // this wave's blocks: kh BPW .. kh BPW + BPW - 1 of the tile
+      f32x4 sc[BPW];
 #pragma unroll
-      for (int b = 0; b < 2 * NK; ++b) {
-        sc[b] = zero4();
-        const T *kr = sK + (16 * b + col) * KROW + G * EL;
+      for (int bl = 0; bl < BPW; ++bl) {
+        sc[bl] = zero4();
+        const T *kr = sK + (16 * (kh * BPW + bl) + col) * KROW + G * EL;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) sc[b] = mfma16(load_frag<T>(kr + s * KW), qf[s], sc[b]);
+        for (int s = 0; s < KS; ++s) sc[bl] = mfma16(load_frag<T>(kr + s * KW), qf[s], sc[bl]);
       }
       // lane holds keys 16 b + 4 G + i of column `row`
-      float x[2 * NK][4];
+      float x[BPW][4];
       float mt = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 2 * NK; ++b)
+      for (int bl = 0; bl < BPW; ++bl)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const int b = kh * BPW + bl;
           const int j = kb + 16 * b + 4 * G + i;
           const bool vis = row_ok && j < k_hi && (j < n_mem || (j - n_mem) <= s_t);
-          x[b][i] = vis ? sc[b][i] * c2 : -INFINITY;
-          mt = fmaxf(mt, x[b][i]);
+          x[bl][i] = vis ? sc[bl][i] * c2 : -INFINITY;
+          mt = fmaxf(mt, x[bl][i]);
         }
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_run == -INFINITY) ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
-      float p[2 * NK][4];
+      float p[BPW][4];
       float ps = 0.f;
 #pragma unroll
-      for (int b = 0; b < 2 * NK; ++b)
+      for (int bl = 0; bl < BPW; ++bl)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[b][i] = (x[b][i] == -INFINITY) ? 0.f : exp2f(x[b][i] - m_new);
-          ps += p[b][i];
+          p[bl][i] = (x[bl][i] == -INFINITY) ? 0.f : exp2f(x[bl][i] - m_new);
+          ps += p[bl][i];
         }
       l_run = l_run * alpha + ps;
       m_run = m_new;
@@ -386,21 +393,22 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
         for (int mb = 0; mb < D / 16; ++mb) {
           const T *vr = sV + (16 * mb + col) * VROW;
 #pragma unroll
-          for (int b = 0; b < 2 * NK; ++b)
+          for (int bl = 0; bl < BPW; ++bl)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              acc_o[mb] = mfma16(Elem<T>::to_f32(vr[16 * b + 4 * G + i]), p[b][i], acc_o[mb]);
+              acc_o[mb] = mfma16(Elem<T>::to_f32(vr[16 * (kh * BPW + bl) + 4 * G + i]), p[bl][i], acc_o[mb]);
         }
       } else {
         // per 32-key k-step ks: k-slots 0..3 <-> keys 32 ks + 4G..+3, slots
         // 4..7 <-> keys 32 ks + 16 + 4G..+3
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
+        for (int ksl = 0; ksl < KSW; ++ksl) {
+          const int ks = kh * KSW + ksl;
           uint32_t w[4];
-          w[0] = (uint32_t)f32_to_bf16(p[2 * ks][0]) | ((uint32_t)f32_to_bf16(p[2 * ks][1]) << 16);
-          w[1] = (uint32_t)f32_to_bf16(p[2 * ks][2]) | ((uint32_t)f32_to_bf16(p[2 * ks][3]) << 16);
-          w[2] = (uint32_t)f32_to_bf16(p[2 * ks + 1][0]) | ((uint32_t)f32_to_bf16(p[2 * ks + 1][1]) << 16);
-          w[3] = (uint32_t)f32_to_bf16(p[2 * ks + 1][2]) | ((uint32_t)f32_to_bf16(p[2 * ks + 1][3]) << 16);
+          w[0] = (uint32_t)f32_to_bf16(p[2 * ksl][0]) | ((uint32_t)f32_to_bf16(p[2 * ksl][1]) << 16);
+          w[1] = (uint32_t)f32_to_bf16(p[2 * ksl][2]) | ((uint32_t)f32_to_bf16(p[2 * ksl][3]) << 16);
+          w[2] = (uint32_t)f32_to_bf16(p[2 * ksl + 1][0]) | ((uint32_t)f32_to_bf16(p[2 * ksl + 1][1]) << 16);
+          w[3] = (uint32_t)f32_to_bf16(p[2 * ksl + 1][2]) | ((uint32_t)f32_to_bf16(p[2 * ksl + 1][3]) << 16);
           const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
           // V^T operand of lane (col, G): dims 16 mb + col, keys 4G..4G+3 and
           // 16+4G..16+4G+3 of the k-step.  ds_read_b64_tr_b16 hands lane i of a
@@ -419,6 +427,29 @@ __global__ __launch_bounds__(64 * WGW) void attend_kernel(AttendArgs a, int n_sp
       }
     }
     __syncthreads();
+  }
+
+  // ---- the two key halves of each row block merge (second half -> LDS -> first)
+  if constexpr (KH > 1) {
+    float *mg = sMerge + (wave * 64 + lane) * (D / 4 + 2);
+    if (kh == 1) {
+      mg[0] = m_run;
+      mg[1] = l_run;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mg[2 + 4 * mb + i] = acc_o[mb][i];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = mg[0], M = fmaxf(m_run, m1);
+    const float w0 = m_run == -INFINITY ? 0.f : exp2f(m_run - M), w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
+    l_run = l_run * w0 + mg[1] * w1;
+    m_run = M;
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_o[mb][i] = acc_o[mb][i] * w0 + mg[2 + 4 * mb + i] * w1;
   }
 
   // ---- epilogue: lane holds dims 16 mb + 4 G + i of row `row` ----------------
@@ -933,6 +964,9 @@ struct Plan {
 // 32-key k-steps per gathered tile of the many-row kernel (64 keys: twice the
 // bytes in flight per round trip of the tile pipeline)
 constexpr int ATT_NK = 2;
+// two waves per row block, each taking one 32-key half of every tile (two
+// waves per SIMD for latency hiding, merged through LDS at the end)
+constexpr int ATT_KH = 2;
 
 Plan plan(const AttendArgs &a) {
   Plan p;
@@ -958,8 +992,8 @@ Plan plan(const AttendArgs &a) {
 template <typename T, int D, int WGW>
 hipError_t launch_kernel(const AttendArgs &a, const Plan &p, const SplitOut &so, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_q * a.h_kv * p.n_rbg * p.n_split;
-  hipLaunchKernelGGL((attend_kernel<T, D, WGW, ATT_NK>), dim3((unsigned)grid), dim3(64 * WGW), 0, s, a, p.n_split,
-                     p.n_rbg, so);
+  hipLaunchKernelGGL((attend_kernel<T, D, WGW, ATT_NK, ATT_KH>), dim3((unsigned)grid), dim3(64 * WGW * ATT_KH), 0, s, a,
+                     p.n_split, p.n_rbg, so);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const int64_t rows = (int64_t)a.n_q * a.T * a.h_q;
