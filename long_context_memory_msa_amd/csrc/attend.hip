@@ -9,11 +9,14 @@
 // (background -> query -> generation causal order).
 //
 // Design (gfx950, flash-attention style, fp32 softmax and accumulation):
-//  * one wave owns 16 query rows of one (query, KV head): rows are
-//    (token, head-in-group) pairs, so GQA heads share every K/V tile;
+//  * a pair of waves owns 16 query rows of one (query, KV head), each wave
+//    one half of every tile's keys, their partial (max, sum, O) merged
+//    through LDS at the end; rows are (token, head-in-group) pairs, so GQA
+//    heads share every K/V tile;
 //  * scores are computed transposed, S^T = K Q^T (keys as MFMA rows), so that
 //    each lane's probabilities are already the B operand of O^T = V^T P^T;
-//  * K/V tiles of 32 keys are gathered into LDS by the workgroup: pooled rows
+//  * K/V tiles of 128 (bf16) or 64 (fp32) keys are gathered into LDS by the
+//    workgroup, each row block's two waves taking one half of them: pooled rows
 //    of the selected documents' chunks in rank order, then local keys rotated
 //    at pos0 + s on the fly; bf16 V rows are stored as they are and read
 //    transposed by ds_read_b64_tr_b16 (gfx950) into the V^T operand, fp32 V
@@ -961,10 +964,11 @@ struct Plan {
   int wgw, n_rb, n_rbg, n_split;
 };
 
-// 32-key k-steps per gathered tile of the many-row kernel (64 keys: twice the
-// bytes in flight per round trip of the tile pipeline)
-constexpr int ATT_NK = 2;
-// two waves per row block, each taking one 32-key half of every tile (two
+// 32-key k-steps per gathered tile of the many-row kernel: bf16 128 keys,
+// fp32 64 (more bytes in flight per round trip of the tile pipeline; fp32's
+// 128-key tile would not fit in LDS)
+template <typename T> constexpr int att_nk() { return sizeof(T) == 2 ? 4 : 2; }
+// two waves per row block, each taking one half of every tile's keys (two
 // waves per SIMD for latency hiding, merged through LDS at the end)
 constexpr int ATT_KH = 2;
 
@@ -992,7 +996,7 @@ Plan plan(const AttendArgs &a) {
 template <typename T, int D, int WGW>
 hipError_t launch_kernel(const AttendArgs &a, const Plan &p, const SplitOut &so, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_q * a.h_kv * p.n_rbg * p.n_split;
-  hipLaunchKernelGGL((attend_kernel<T, D, WGW, ATT_NK, ATT_KH>), dim3((unsigned)grid), dim3(64 * WGW * ATT_KH), 0, s, a,
+  hipLaunchKernelGGL((attend_kernel<T, D, WGW, att_nk<T>(), ATT_KH>), dim3((unsigned)grid), dim3(64 * WGW * ATT_KH), 0, s, a,
                      p.n_split, p.n_rbg, so);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
