@@ -603,7 +603,10 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
   __shared__ int64_t sCB[MAX_K];             // first chunk of each selected document
   __shared__ int32_t sDoc[MAX_K];
   __shared__ int64_t sList[DPASS];           // chunk of each memory key of the pass (-1 - s: local key s)
-  __shared__ float sPr[DW][16][GQ + 1];      // a wave's block probabilities [key][head]
+  constexpr bool PV_MFMA = sizeof(T) == 2;   // bf16: O^T += V^T P^T on MFMA; fp32: on the vector units
+  constexpr int VP = D + 8;                  // LDS pitch of a wave's V block (elements)
+  __shared__ __align__(16) T sVb[PV_MFMA ? DW : 1][PV_MFMA ? 16 * VP : 1];  // a wave's 16 V rows
+  __shared__ float sPr[PV_MFMA ? 1 : DW][16][GQ + 1];  // a wave's block probabilities [key][head]
   __shared__ float sAl[DW][GQ];              // and its rescale factors per head
   __shared__ float sM[DW][GQ], sL[DW][GQ];
   __shared__ float sAcc[DW][GQ][D];
@@ -739,11 +742,14 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
   const T *vbar = static_cast<const T *>(a.vbar) + (int64_t)kvh * a.kv_stride * D;
   const float c2 = a.scale * LOG2E;
   float m_run = -INFINITY, l_run = 0.f;  // column col's running max; this lane's share of its sum
-  float acc[GQ][EPL];
+  float acc[GQ][EPL];  // vector path: O[h][dims e0 ..] of this lane's key slots
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  f32x4 oacc[D / 16];  // MFMA path: O^T tile mb, lane (head col, G): dims 16 mb + 4 G .. + 3
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) oacc[mb] = zero4();
 
   for (int pb = 0; pb < n_keys; pb += DPASS) {
     const int np = min(DPASS, n_keys - pb);
@@ -793,7 +799,7 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int kb = (b0 + nb * VW) * 16;
-        if (b0 + nb * VW >= n_blk) break;  // wave-uniform
+        if (b0 + nb * VW < n_blk) {  // wave-uniform (a predicate, not a break: the indices stay constant)
         // local keys: RoPE at pos0 + s (partner dims are k-step st + KS/2 of this lane)
         {
           const int jl = kb + col;
@@ -833,38 +839,65 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m_run, mt);
         const float alpha = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
-        float ps = 0.f;
+        float pr4[4], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pr = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
-          ps += pr;
-          if (col < GQ) sPr[wave][4 * G + i][col] = pr;
+          pr4[i] = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
+          ps += pr4[i];
         }
-        if (col < GQ && G == 0) sAl[wave][col] = alpha;
         l_run = l_run * alpha + ps;
         m_run = m_new;
-        wave_sync();
-        // O[h][dims] += p[key][h] V[key][dims] for this lane's keys vr + KPI u
-        float al[GQ];
+        if constexpr (PV_MFMA) {
+          // P^T (B operand): lane (head col, G) holds keys 4G..4G+3 of its
+          // column, exactly the scores' layout; V rows go to the wave's LDS
+          // slot as they are and come back transposed (ds_read_b64_tr_b16:
+          // lane a of group G addresses key 4G + a/4, dims 16 mb + 4 (a % 4)
+          // and receives dims 16 mb + a of keys 4G .. 4G+3: the V^T operand)
+          T *slot = sVb[wave];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) al[h] = sAl[wave][h];
+          for (int u = 0; u < VPB; ++u) {  // (field by field: an aggregate copy keeps vw out of registers)
+            const uint32_t w0 = vw[nb][u].x, w1 = vw[nb][u].y, w2 = vw[nb][u].z, w3 = vw[nb][u].w;
+            *reinterpret_cast<uint4 *>(slot + (vr + KPI * u) * VP + e0) = uint4{w0, w1, w2, w3};
+          }
+          const uint32_t p01 = (uint32_t)f32_to_bf16(pr4[0]) | ((uint32_t)f32_to_bf16(pr4[1]) << 16);
+          const uint32_t p23 = (uint32_t)f32_to_bf16(pr4[2]) | ((uint32_t)f32_to_bf16(pr4[3]) << 16);
+          const v4i16 pb = __builtin_bit_cast(v4i16, uint2{p01, p23});
+          wave_sync();
+          const T *vb = slot + (4 * G + col / 4) * VP + 4 * (col % 4);
 #pragma unroll
-        for (int h = 0; h < GQ; ++h)
+          for (int mb = 0; mb < D / 16; ++mb) {
+            const v4i16 vt = lds_read_tr16(vb + 16 * mb);
+            oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb, oacc[mb] * alpha, 0, 0, 0);
+          }
+        } else {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
+          for (int i = 0; i < 4; ++i)
+            if (col < GQ) sPr[wave][4 * G + i][col] = pr4[i];
+          if (col < GQ && G == 0) sAl[wave][col] = alpha;
+          wave_sync();
+          // O[h][dims] += p[key][h] V[key][dims] for this lane's keys vr + KPI u
+          float al[GQ];
 #pragma unroll
-        for (int u = 0; u < VPB; ++u) {
-          float v[EPL];
-          unpack16<T>(vw[nb][u], v);
-          const int key = vr + KPI * u;
+          for (int h = 0; h < GQ; ++h) al[h] = sAl[wave][h];
 #pragma unroll
-          for (int h = 0; h < GQ; ++h) {
-            const float pr = sPr[wave][key][h];
+          for (int h = 0; h < GQ; ++h)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr, v[e], acc[h][e]);
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
+#pragma unroll
+          for (int u = 0; u < VPB; ++u) {
+            float v[EPL];
+            unpack16<T>(vw[nb][u], v);
+            const int key = vr + KPI * u;
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+              const float prh = sPr[wave][key][h];
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(prh, v[e], acc[h][e]);
+            }
           }
         }
         wave_sync();  // the slot is read before the next block rewrites it
+        }
       }
     };
     for (int b0 = split * DW + wave; b0 < n_blk; b0 += VW * NB) {
@@ -879,17 +912,26 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
   // the wave's totals: the sum over its lanes of each column, O over its key slots
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+  if (lane < GQ) {  // lanes 0..GQ-1: column = head, G = 0
+    sM[wave][lane] = m_run;
+    sL[wave][lane] = l_run;
+  }
+  if constexpr (PV_MFMA) {
+    if (col < GQ) {  // lane (head col, G) holds dims 16 mb + 4 G + i
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sAcc[wave][col][16 * mb + 4 * G + i] = oacc[mb][i];
+    }
+  } else {
 #pragma unroll
   for (int o = LPK; o < 64; o <<= 1)
 #pragma unroll
     for (int h = 0; h < GQ; ++h)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
-  if (lane < GQ) {  // lanes 0..GQ-1: column = head, G = 0
-    sM[wave][lane] = m_run;
-    sL[wave][lane] = l_run;
   }
-  if (lane < LPK) {
+  if (!PV_MFMA && lane < LPK) {
 #pragma unroll
     for (int h = 0; h < GQ; ++h)
 #pragma unroll
