@@ -17,8 +17,11 @@ independent batches through the decode pipeline (two route streams whose
 scans overlap, the top-k and attention of earlier batches on a third); the
 pipelined rate is the throughput `value`.  The same line carries the Memory
 Interleave workload (18 routed layers x 10M-token banks, 3 rounds; MFMA-bound)
-as the `interleave` record, and the fp64 oracle's rate on the host's cores as
-`cpu_baseline` (timed first, before the GPU is used).  Prints one JSON line.
+as the `interleave` record, the tiered bank (Kbar/Vbar in pinned host memory,
+pipelined decode), the incremental append of the last 10% of the documents and
+the router projector GEMM as the `tiered`, `append` and `project` records, and
+the fp64 oracle's rate on the host's cores as `cpu_baseline` (timed first,
+before the GPU is used).  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -334,7 +337,7 @@ def bench_interleave(args) -> int:
     return 0
 
 
-def bench_project(args) -> int:
+def project_measure(args) -> dict:
     """Router projection GEMM (Y = X W^T, bf16, fp32 accumulation): the
     encoding-time projection of a 256K-token slab of memory hidden states
     (hidden 2560 -> router 4 x 256) and the decode-time projection of 16 query
@@ -375,11 +378,10 @@ def bench_project(args) -> int:
         "cases": res,
         "data": "synthetic",
     }
-    print(json.dumps(rec), flush=True)
-    return 0
+    return rec
 
 
-def bench_append(args) -> int:
+def append_measure(args) -> dict:
     """Incremental update of the 100M-token bank: encode the first 90% of the
     documents into a bank with room for all, append the rest, pool only the
     appended range; report the pooling rate of the appended range and the
@@ -450,11 +452,10 @@ def bench_append(args) -> int:
         "gold_recovered_after": gold_ok,
         "data": "synthetic",
     }
-    print(json.dumps(rec), flush=True)
-    return 0
+    return rec
 
 
-def bench_tiered(args) -> int:
+def tiered_measure(args) -> dict:
     """The 100M-token decode layer with a tiered bank: pooled keys/values in
     pinned host memory (read by the attention over the host link), router keys
     in HBM.  Steps of the same query batch run through the decode pipeline
@@ -542,7 +543,12 @@ def bench_tiered(args) -> int:
         "hbm_bytes": bank.bytes_resident(),
         "host_bytes": bank.kbar.numel() * bank.kbar.element_size() * 2,
     }
-    print(json.dumps(rec), flush=True)
+    return rec
+
+
+def bench_secondary(args, measure) -> int:
+    """A secondary workload's own line (not the headline)."""
+    print(json.dumps(measure(args)), flush=True)
     return 0
 
 
@@ -565,6 +571,8 @@ def main() -> int:
                          "appended to an encoded bank; project: the router projection GEMM")
     ap.add_argument("--no-interleave", action="store_true",
                     help="decode: leave out the Memory Interleave sub-record (18 layers x 10M tokens)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="decode: leave out the tiered-bank, append and projector sub-records")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -607,11 +615,11 @@ def main() -> int:
     if args.workload == "interleave":
         return bench_interleave(args)
     if args.workload == "tiered":
-        return bench_tiered(args)
+        return bench_secondary(args, tiered_measure)
     if args.workload == "append":
-        return bench_append(args)
+        return bench_secondary(args, append_measure)
     if args.workload == "project":
-        return bench_project(args)
+        return bench_secondary(args, project_measure)
     w = W.make_workload("decode-100m", bank_tokens=args.bank_tokens)
     print(f"[bench] {w.name}: {w.n_tok} tokens, {w.n_docs} docs, {w.n_chunks} chunks", file=sys.stderr, flush=True)
 
@@ -735,12 +743,21 @@ def main() -> int:
         "pool": {"slabs": enc["slabs"], "GB/s": pool_gbs, "frac": pool_gbs / HBM_PEAK_GBS},
         "gold_recovered": gold_ok,
     }
-    if not args.no_interleave:
-        # the MFMA-bound workload beside the headline (its own banks; the
-        # decode bank is released first)
-        del bank, ws
+    if not (args.no_interleave and args.no_secondary):
+        del bank, ws  # the sub-records below build their own banks and inputs
         torch.cuda.empty_cache()
+    if not args.no_interleave:
+        # the MFMA-bound workload beside the headline
         rec["interleave"] = interleave_measure(args, 3)
+    if not args.no_secondary:
+        # the host-tier bank, incremental append and router projector rows;
+        # the headline fields above are not touched
+        for name, measure in (("tiered", tiered_measure), ("append", append_measure),
+                              ("project", project_measure)):
+            print(f"[bench] {name} ...", file=sys.stderr, flush=True)
+            sub = measure(args)
+            torch.cuda.empty_cache()
+            rec[name] = {k: v for k, v in sub.items() if k not in ("n_gpus", "steps", "warmup", "dtype", "data")}
     if cpu_rec is not None:
         rec["cpu_baseline"] = cpu_rec
     print(json.dumps(rec), flush=True)
