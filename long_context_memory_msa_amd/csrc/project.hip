@@ -9,14 +9,20 @@
 // accumulation.
 //
 // A bf16 GEMM with both operands contiguous along K:
-//  * a workgroup owns 128 rows x 128 outputs; four waves of 64 x 64 on
-//    v_mfma_f32_16x16x32_bf16;
+//  * a workgroup owns 256 rows x 256 outputs (sixteen waves of 64 x 64 on
+//    v_mfma_f32_16x16x32_bf16, four per SIMD: a 256K x 2560 x 1024 slab at
+//    40 % of the bf16 MFMA peak against 33 % for 128 x 128 tiles of four waves
+//    at two workgroups per CU, and 28-30 % for 256 x 128 or 128 x 256 tiles of
+//    eight waves), or 128 x 128 where the outputs are not a multiple of 256 or
+//    the rows few;
 //  * the K loop runs in stages of 64 elements (128 bytes per row) filled by
 //    direct-to-LDS loads into swizzled rows, double-buffered (separate LDS
 //    variables per buffer, so the compiler does not wait for the fill in
 //    flight), one barrier per stage;
 //  * output tiles of one row tile share an XCD (blockIdx % 8), so the row
-//    tile is re-read from that XCD's L2.
+//    tile is re-read from that XCD's L2;
+//  * the product is taken as W X^T, so that a lane's accumulator holds four
+//    consecutive outputs of one row: 8-byte stores.
 //
 // A few rows (a decode step's queries) leave that tiling with out/128
 // workgroups walking the whole K loop one after another; there the product is
@@ -35,7 +41,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int PT = 128;  // rows (and outputs) per workgroup
 constexpr int SK = 64;   // K elements per stage
 // row counts up to this take the skinny kernel (at most 4 row tiles of 16)
 constexpr int SKINNY_ROWS = 64;
@@ -56,10 +61,13 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-__global__ __launch_bounds__(256, 2) void project_kernel(const bf16_t *X, const bf16_t *W, int64_t rows, int hidden,
+// PM rows x PN outputs per workgroup, waves of 64 x 64
+template <int PM, int PN, int PW = (PM / 64) * (PN / 64)>
+__global__ __launch_bounds__(64 * PW) void project_kernel(const bf16_t *X, const bf16_t *W, int64_t rows, int hidden,
                                                          int out, bf16_t *Y, int n_rtiles, int n_otiles) {
-  __shared__ __align__(16) bf16_t sA0[PT * SK], sA1[PT * SK];
-  __shared__ __align__(16) bf16_t sB0[PT * SK], sB1[PT * SK];
+  __shared__ __align__(16) bf16_t sA0[PM * SK], sA1[PM * SK];
+  __shared__ __align__(16) bf16_t sB0[PN * SK], sB1[PN * SK];
+  constexpr int FA = PM / PW / 8, FB = PN / PW / 8;  // 1 KB direct-to-LDS loads per wave per stage
 
   // tile order: output tiles of one row tile share blockIdx % 8 (one XCD)
   const int b = blockIdx.x;
@@ -70,30 +78,34 @@ __global__ __launch_bounds__(256, 2) void project_kernel(const bf16_t *X, const 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, G = lane >> 4;
-  const int wr = wave & 1, wc = wave >> 1;
-  const int64_t row0 = (int64_t)r_tile * PT;
-  const int o0 = o_tile * PT;
-  const int rows_here = (int)std::min<int64_t>(PT, rows - row0);
+  const int wr = wave % (PM / 64), wc = wave / (PM / 64);
+  const int64_t row0 = (int64_t)r_tile * PM;
+  const int o0 = o_tile * PN;
+  const int rows_here = (int)std::min<int64_t>(PM, rows - row0);
   const bf16_t *xt = X + row0 * hidden;
   const bf16_t *wt = W + (int64_t)o0 * hidden;
 
   // fill of a stage: wave w writes rows 32w .. 32w+31 of each operand; in load
   // p, lane L writes row 32w + 8p + L/8 at physical slot L%8 = logical slot
   // (L%8) ^ swz(row); rows past the end read the last valid row (discarded)
-  uint32_t aoff[4], boff[4];
+  uint32_t aoff[FA], boff[FB];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int row = 32 * wave + 8 * p + lane / 8;
+  for (int p = 0; p < FA; ++p) {
+    const int row = 8 * FA * wave + 8 * p + lane / 8;
     const int slot = (lane % 8) ^ swz(row);
     aoff[p] = (uint32_t)(std::min(row, rows_here - 1) * hidden + slot * 8);
+  }
+#pragma unroll
+  for (int p = 0; p < FB; ++p) {
+    const int row = 8 * FB * wave + 8 * p + lane / 8;
+    const int slot = (lane % 8) ^ swz(row);
     boff[p] = (uint32_t)(row * hidden + slot * 8);
   }
   auto fill = [&](bf16_t *dA, bf16_t *dB, int k0) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      fill16(xt + aoff[p] + k0, dA + (32 * wave + 8 * p) * SK);
-      fill16(wt + boff[p] + k0, dB + (32 * wave + 8 * p) * SK);
-    }
+    for (int p = 0; p < FA; ++p) fill16(xt + aoff[p] + k0, dA + (8 * FA * wave + 8 * p) * SK);
+#pragma unroll
+    for (int p = 0; p < FB; ++p) fill16(wt + boff[p] + k0, dB + (8 * FB * wave + 8 * p) * SK);
   };
   f32x4 acc[4][4];
 #pragma unroll
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void project_kernel(const bf16_t *X, const 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fb[j], fa[i], acc[i][j]);
     }
   };
 
@@ -133,18 +145,20 @@ __global__ __launch_bounds__(256, 2) void project_kernel(const bf16_t *X, const 
     }
   }
 
-  // acc[i][j]: rows 64 wr + 16 i + 4 G + e, outputs 64 wc + 16 j + col
+  // acc[i][j]: outputs 64 wc + 16 j + 4 G + e of row 64 wr + 16 i + col (8 bytes per lane)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * wr + 16 * i + col;
+    if (r < rows_here) {
+      bf16_t *yrow = Y + (row0 + r) * out + o0 + 64 * wc + 4 * G;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 64 * wr + 16 * i + 4 * G + e;
-      if (r < rows_here) {
-        bf16_t *yrow = Y + (row0 + r) * out + o0 + 64 * wc + col;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) yrow[16 * j] = bf16_t{f32_to_bf16(acc[i][j][e])};
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(acc[i][j][0]) | ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(acc[i][j][2]) | ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2 *>(yrow + 16 * j) = uint2{w0, w1};
       }
     }
+  }
 }
 
 // rows <= 16 * MT; grid = out / 16 workgroups of 8 waves
@@ -211,6 +225,16 @@ void launch_skinny(const void *X, const void *W, int rows, int hidden, int out, 
                      static_cast<const bf16_t *>(W), rows, hidden, out, static_cast<bf16_t *>(Y));
 }
 
+template <int PM, int PN>
+hipError_t launch_tiled(const void *X, const void *W, int64_t rows, int hidden, int out, void *Y, hipStream_t s) {
+  const int n_rtiles = (int)((rows + PM - 1) / PM), n_otiles = out / PN;
+  const int64_t grid = 8 * (int64_t)n_otiles * ((n_rtiles + 7) / 8);
+  hipLaunchKernelGGL((project_kernel<PM, PN>), dim3((unsigned)grid), dim3(64 * (PM / 64) * (PN / 64)), 0, s,
+                     static_cast<const bf16_t *>(X), static_cast<const bf16_t *>(W), rows, hidden, out,
+                     static_cast<bf16_t *>(Y), n_rtiles, n_otiles);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_project(const void *X, const void *W, int64_t rows, int hidden, int out, void *Y, hipStream_t s) {
@@ -223,11 +247,11 @@ hipError_t launch_project(const void *X, const void *W, int64_t rows, int hidden
     else launch_skinny<4>(X, W, r, hidden, out, Y, s);
     return hipGetLastError();
   }
-  const int n_rtiles = (int)((rows + PT - 1) / PT), n_otiles = out / PT;
-  const int64_t grid = 8 * (int64_t)n_otiles * ((n_rtiles + 7) / 8);
-  hipLaunchKernelGGL(project_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(X),
-                     static_cast<const bf16_t *>(W), rows, hidden, out, static_cast<bf16_t *>(Y), n_rtiles, n_otiles);
-  return hipGetLastError();
+  // 256 x 256 tiles (sixteen waves, four per SIMD, one workgroup per CU)
+  // where the outputs and rows fill them; 128 x 128 (four waves, two
+  // workgroups per CU) otherwise
+  if (out % 256 == 0 && rows >= 1024) return launch_tiled<256, 256>(X, W, rows, hidden, out, Y, s);
+  return launch_tiled<128, 128>(X, W, rows, hidden, out, Y, s);
 }
 
 }  // namespace msa

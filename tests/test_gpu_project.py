@@ -50,10 +50,13 @@ def _check_projection(X, Wt, Y):
 
 
 # rows <= 64 take the skinny kernel (1-4 row tiles, K split over 8 waves, batches of
-# 4 or 8 k-steps with a ragged last batch); more rows take the 128 x 128 tiles
+# 4 or 8 k-steps with a ragged last batch); more rows take the 128 x 128 tiles, and
+# from 1024 rows with outputs a multiple of 256 the 256 x 256 tiles (ragged last
+# row tile: 1025, 4099)
 @pytest.mark.parametrize("rows,hidden,out", [(1, 64, 128), (16, 2560, 1024), (17, 192, 128), (33, 320, 256),
                                              (48, 2560, 1024), (64, 704, 384), (65, 2560, 1024), (200, 640, 256),
-                                             (1000, 128, 384), (4099, 2560, 1024)])
+                                             (1000, 128, 384), (1025, 128, 512), (2048, 320, 768),
+                                             (2000, 192, 384), (4099, 2560, 1024)])
 def test_project_isolated(device, rows, hidden, out):
     log(f"project rows={rows} hidden={hidden} out={out}")
     X = W.hidden_states(3, rng.ROLE_HID_MEM, rows, hidden)
