@@ -182,14 +182,35 @@ __global__ __launch_bounds__(2 * NW, 2) void route_wide_kernel(RouteArgs a, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) score[i][j] = zero4();
 
-  // scales of the tile's rows and chunks (qinv is [h][n_rows], kr_inv_norm [chunk][h])
-  for (int k = tid; k < MW * HR; k += NT) {
-    const int h = k / MW, row = k % MW;
-    sqi[h][row] = row < rows_here ? a.qinv[(int64_t)h * n_rows + row0 + row] : 0.f;
-  }
-  for (int k = tid; k < NW * HR; k += NT) {
-    const int c = k / HR, h = k % HR;
-    sik[h][c] = c < chunks_here ? a.kr_inv_norm[(c0 + c) * HR + h] : 0.f;
+  // scales of the tile's rows and chunks (qinv is [h][n_rows], kr_inv_norm
+  // [chunk][h]), every load in flight before the first LDS write
+  {
+    constexpr int SQ = (MW * HR + NT - 1) / NT, SC = (NW * HR + NT - 1) / NT;
+    float vq[SQ], vc[SC];
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+      const int k = tid + i * NT, h = k / MW, row = k % MW;
+      const bool ok = k < MW * HR && row < rows_here;
+      vq[i] = a.qinv[ok ? (int64_t)h * n_rows + row0 + row : 0];
+      if (!ok) vq[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < SC; ++i) {
+      const int k = tid + i * NT, c = k / HR, h = k % HR;
+      const bool ok = k < NW * HR && c < chunks_here;
+      vc[i] = a.kr_inv_norm[ok ? (c0 + c) * HR + h : 0];
+      if (!ok) vc[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+      const int k = tid + i * NT;
+      if (k < MW * HR) sqi[k / MW][k % MW] = vq[i];
+    }
+#pragma unroll
+    for (int i = 0; i < SC; ++i) {
+      const int k = tid + i * NT;
+      if (k < NW * HR) sik[k % HR][k / HR] = vc[i];
+    }
   }
   const int mydoc = tid < chunks_here ? a.chunk_doc[c0 + tid] : -1;  // document of chunk tid (tid < NW)
   fill(sA0, sB0, rot, 0);
@@ -348,13 +369,27 @@ __global__ __launch_bounds__(64 * RW_WAVES, 1) void route_rows_kernel(RouteArgs 
     for (int st = 0; st < KS; ++st) ring[p][st] = load_frag<bf16_t>(kp_cur + p * DR + st * KW);
   load_meta(t0, ik_cur, doc_cur);
 
-  // query fragments of the row blocks in MFMA A-operand order, and their norms
-  for (int e = threadIdx.x; e < RB * NF * 64; e += 64 * RW_WAVES) {
-    const int r = e / (NF * 64), f = (e / 64) % NF, l = e % 64, h = f / KS, st = f % KS;
-    const int row = r * 16 + (l & 15);
-    bf16x8 v = bf16x8{};
-    if (row < n_rows) v = load_frag<bf16_t>(qr + ((int64_t)row * HR + h) * DR + st * KW + (l >> 4) * EL);
-    qfrag[r][f][l] = v;
+  // query fragments of the row blocks in MFMA A-operand order, and their
+  // norms: every load in flight before the first is written to LDS (one
+  // round trip at a time had cost ~9 us per call)
+  {
+    constexpr int QPT = (RB * NF * 64 + 64 * RW_WAVES - 1) / (64 * RW_WAVES);
+    bf16x8 qt[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int e = threadIdx.x + i * 64 * RW_WAVES;
+      const int r = e / (NF * 64), f = (e / 64) % NF, l = e % 64, h = f / KS, st = f % KS;
+      const int row = r * 16 + (l & 15);
+      const bool ok = e < RB * NF * 64 && row < n_rows;
+      const int64_t src = ok ? ((int64_t)row * HR + h) * DR + st * KW + (l >> 4) * EL : 0;  // row 0: a valid address
+      qt[i] = load_frag<bf16_t>(qr + src);
+      if (!ok) qt[i] = bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int e = threadIdx.x + i * 64 * RW_WAVES;
+      if (e < RB * NF * 64) qfrag[e / (NF * 64)][(e / 64) % NF][e % 64] = qt[i];
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < RB * HR * 16; e += 64 * RW_WAVES) {
