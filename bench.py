@@ -746,18 +746,22 @@ def main() -> int:
     if not (args.no_interleave and args.no_secondary):
         del bank, ws  # the sub-records below build their own banks and inputs
         torch.cuda.empty_cache()
+    # the secondary workloads run after the headline is measured; one that
+    # raises records its error in its own field instead of losing the line
+    subs = []
     if not args.no_interleave:
-        # the MFMA-bound workload beside the headline
-        rec["interleave"] = interleave_measure(args, 3)
+        subs.append(("interleave", lambda a: interleave_measure(a, 3)))   # the MFMA-bound workload
     if not args.no_secondary:
-        # the host-tier bank, incremental append and router projector rows;
-        # the headline fields above are not touched
-        for name, measure in (("tiered", tiered_measure), ("append", append_measure),
-                              ("project", project_measure)):
-            print(f"[bench] {name} ...", file=sys.stderr, flush=True)
+        subs += [("tiered", tiered_measure), ("append", append_measure), ("project", project_measure)]
+    for name, measure in subs:
+        print(f"[bench] {name} ...", file=sys.stderr, flush=True)
+        try:
             sub = measure(args)
-            torch.cuda.empty_cache()
             rec[name] = {k: v for k, v in sub.items() if k not in ("n_gpus", "steps", "warmup", "dtype", "data")}
+        except Exception as exc:  # noqa: BLE001 -- reported on the line, the headline stands
+            rec[name] = {"error": f"{type(exc).__name__}: {exc}"}
+            print(f"[bench] {name} failed: {exc!r}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     if cpu_rec is not None:
         rec["cpu_baseline"] = cpu_rec
     print(json.dumps(rec), flush=True)
