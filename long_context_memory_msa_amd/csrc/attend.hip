@@ -564,10 +564,13 @@ __device__ __forceinline__ void from_frag(const typename Frag<T>::type &f, float
 //    block's scores S^T = K Q^T come from MFMAs whose A operand is loaded
 //    straight from the key rows (lane: key l % 16, 16 bytes per k-step), Q^T
 //    in registers (column = query head);
-//  * the running softmax is kept per column; the block's probabilities go to
-//    a small LDS slot of the wave, from which the value side reads them;
-//  * values are read in row layout (a key row spread over LPK lanes, 16 bytes
-//    each) and accumulated in fp32 on the vector units, O[h][dims] per lane;
+//  * the running softmax is kept per column; values are read in row layout
+//    (a key row spread over LPK lanes, 16 bytes each);
+//  * bf16: O^T += V^T P^T on MFMA (16x16x16): the block's probabilities are
+//    the B operand in the scores' own lane layout, and the block's V rows go
+//    to a per-wave LDS slot as they are and come back transposed
+//    (ds_read_b64_tr_b16); fp32: the probabilities go through the wave's LDS
+//    slot and O[h][dims] accumulates on the vector units;
 //  * loads for NB blocks are in flight before any of them is used;
 //  * the waves' (max, sum, O) are merged through LDS; with ns > 1 the
 //    workgroups' merged partials go to attend_combine_kernel.
