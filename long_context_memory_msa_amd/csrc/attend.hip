@@ -488,20 +488,41 @@ __global__ __launch_bounds__(64 * WGW * KH) void attend_kernel(AttendArgs a, int
 }
 
 // Log-sum-exp merge of the split partials: one thread per (row, dim).
+// Splits are taken CS at a time with all of a group's loads in flight (a
+// loop over the splits would wait for each load in turn); groups after the
+// first fold in by the same log-sum-exp rescaling.
+constexpr int CS = 8;
 template <typename T, int D>
 __global__ void attend_combine_kernel(int64_t rows, int n_split, SplitOut so, void *O) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= rows * D) return;
   const int64_t r = e / D;
   const int dd = (int)(e % D);
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, so.m[r * n_split + s]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float ms = so.m[r * n_split + s];
-    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    L += w * so.l[r * n_split + s];
-    acc += w * so.o[(r * n_split + s) * D + dd];
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += CS) {
+    float mv[CS], lv[CS], ov[CS];
+#pragma unroll
+    for (int i = 0; i < CS; ++i) {
+      const int64_t k = r * n_split + min(s0 + i, n_split - 1);  // past the last split: re-read it, unused
+      mv[i] = so.m[k];
+      lv[i] = so.l[k];
+      ov[i] = so.o[k * D + dd];
+    }
+    float Mg = M;
+#pragma unroll
+    for (int i = 0; i < CS; ++i)
+      if (s0 + i < n_split) Mg = fmaxf(Mg, mv[i]);
+    const float sc = M == -INFINITY ? 0.f : exp2f(M - Mg);  // (L and acc are 0 while M is -inf)
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < CS; ++i)
+      if (s0 + i < n_split) {
+        const float w = mv[i] == -INFINITY ? 0.f : exp2f(mv[i] - Mg);
+        L += w * lv[i];
+        acc += w * ov[i];
+      }
+    M = Mg;
   }
   static_cast<T *>(O)[r * D + dd] = Elem<T>::from_f32(acc / L);
 }
