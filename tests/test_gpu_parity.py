@@ -270,10 +270,11 @@ def test_attend_all_documents_is_dense(device):
 
 @pytest.mark.parametrize("name,T,L_loc", [("prefill-16k", 1, 1), ("prefill-16k", 1, 37), ("prefill-16k", 3, 70),
                                            ("prefill-16k", 50, 50), ("prefill-16k", 64, 640),
-                                           ("tiny-f32", 40, 90), ("tiny-f32", 3, 130)])
+                                           ("prefill-16k", 3, 640), ("tiny-f32", 40, 90), ("tiny-f32", 3, 130)])
 def test_attend_shapes(device, name, T, L_loc):
     # decode and partial prefill over long local contexts (causal tails, several
-    # key tiles; fp32: four-row-block and one-row-block workgroups)
+    # key tiles; fp32: four-row-block and one-row-block workgroups; 3 tokens over
+    # 640 local keys: ten key splits, merged eight at a time then two)
     w = _wl(name)
     w = dataclasses.replace(w, T=T, L_loc=L_loc, T_route=min(L_loc, 128), rounds=1, append=0)
     idx_h = np.random.default_rng(T + L_loc).choice(w.n_docs, size=(1, w.k), replace=False)
