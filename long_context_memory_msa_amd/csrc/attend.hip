@@ -625,7 +625,6 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
 
   __shared__ int32_t sP[MAX_K + 1];          // prefix of the selected documents' chunk counts
   __shared__ int64_t sCB[MAX_K];             // first chunk of each selected document
-  __shared__ int32_t sDoc[MAX_K];
   __shared__ int64_t sList[DPASS];           // chunk of each memory key of the pass (-1 - s: local key s)
   constexpr bool PV_MFMA = sizeof(T) == 2;   // bf16: O^T += V^T P^T on MFMA; fp32: on the vector units
   constexpr int VP = D + 8;                  // LDS pitch of a wave's V block (elements)
@@ -700,62 +699,66 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
     for (int st = 0; st < KS; ++st) qf[st] = to_frag<T>(x[st]);
   }
 
-  // selected documents: the layer's in-kernel selection, or idx
+  // selected documents: the layer's in-kernel selection, or idx; wave 0
+  // then loads their chunk ranges (ranks r = lane + 64 j, all loads issued
+  // before the first is used) and forms the prefix of the counts with wave
+  // scans, so one barrier publishes the list (an id outside [0, n_docs)
+  // makes the query's output NaN)
   if (wave == 0) {
-    if (a.cand) {
+    constexpr int RPL = MAX_K / 64;  // ranks per lane
+    int doc[RPL];
+    if (a.cand) {  // (k <= 64: the rank-r winner is in lane r)
 #pragma unroll
       for (int j = 0; j < CI; ++j) cv[j] = j < c_run && lane * c_run + j < a.n_cand ? cv[j] : 0;
       const uint64_t e = wave_topk_sorted_fast<CI>(cv, (uint32_t)a.k, sHist, sSel);
-      if (lane < a.k) {
-        sDoc[lane] = (int)(0xFFFFFFFFu - (uint32_t)e);
-        if (a.idx_out && kvh == 0 && split == 0) {
-          a.idx_out[(int64_t)q * a.k + lane] = sDoc[lane];
-          a.val_out[(int64_t)q * a.k + lane] = key_score((uint32_t)(e >> 32));
-        }
+      doc[0] = (int)(0xFFFFFFFFu - (uint32_t)e);
+      if (lane < a.k && a.idx_out && kvh == 0 && split == 0) {
+        a.idx_out[(int64_t)q * a.k + lane] = doc[0];
+        a.val_out[(int64_t)q * a.k + lane] = key_score((uint32_t)(e >> 32));
       }
+#pragma unroll
+      for (int j = 1; j < RPL; ++j) doc[j] = 0;
     } else {
-      for (int r = lane; r < a.k; r += 64) sDoc[r] = a.idx[(int64_t)q * a.k + r];
-    }
-    if (lane == 0) sBad = 0;
-  }
-  __syncthreads();
-  // chunk ranges of the selected documents (an id outside [0, n_docs) makes
-  // the query's output NaN)
-  for (int r = tid; r < a.k; r += NT) {
-    const int doc = sDoc[r];
-    if (doc < 0 || doc >= a.n_docs) {
-      sBad = 1;
-      sCB[r] = 0;
-      sP[r] = 0;
-    } else {
-      const int64_t c0 = a.doc_chunk_off[doc];
-      sCB[r] = c0;
-      sP[r] = (int)(a.doc_chunk_off[doc + 1] - c0);
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {  // exclusive prefix of the counts, 4 ranks per lane (k <= 256)
-    int c[4], sum = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * lane + j;
-      c[j] = r < a.k ? sP[r] : 0;
-      sum += c[j];
+      for (int j = 0; j < RPL; ++j) {
+        const int r = lane + 64 * j;
+        doc[j] = r < a.k ? a.idx[(int64_t)q * a.k + r] : 0;
+      }
     }
-    int x = sum;
+    bool any_bad = false;
+    int64_t c0[RPL];
+    int64_t c1[RPL];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
+    for (int j = 0; j < RPL; ++j) {
+      const int r = lane + 64 * j;
+      const bool bad_doc = r < a.k && (doc[j] < 0 || doc[j] >= a.n_docs);
+      any_bad |= bad_doc;
+      const int d = r < a.k && !bad_doc ? doc[j] : 0;
+      c0[j] = a.doc_chunk_off[d];
+      c1[j] = a.doc_chunk_off[d + 1];
     }
-    int run = x - sum;
+    int carry = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * lane + j;
-      if (r < a.k) sP[r] = run;
-      run += c[j];
+    for (int j = 0; j < RPL; ++j) {
+      const int r = lane + 64 * j;
+      const int cnt = r < a.k ? (int)(c1[j] - c0[j]) : 0;
+      int x = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (r < a.k) {
+        sCB[r] = c0[j];
+        sP[r] = carry + x - cnt;
+      }
+      carry += __shfl(x, 63, 64);
     }
-    if (lane == 63) sP[a.k] = x;
+    const bool bad_any = __ballot(any_bad) != 0;
+    if (lane == 0) {
+      sP[a.k] = carry;
+      sBad = bad_any ? 1 : 0;
+    }
   }
   __syncthreads();
   const bool bad = sBad != 0;

@@ -724,6 +724,22 @@ def test_attend_single_token_heads(device, name, h_kv, h_q, L_loc):
     assert_attention_close(got, want)
 
 
+# single-token queries selecting more than 64 documents: the decode kernel's
+# chunk prefix over several groups of 64 ranks, memory keys over several
+# 1,024-key passes, k up to the ABI's 256
+@pytest.mark.parametrize("k", [100, 256])
+def test_attend_single_token_many_documents(device, k):
+    w = _wl("prefill-1m", 600_000)
+    n_q = 3
+    assert w.n_docs >= k
+    w = dataclasses.replace(w, n_q=n_q, T=1, L_loc=9, T_route=1, k=k, pos0=k, gold=np.zeros((n_q, 0), np.int64))
+    g = np.random.default_rng(k)
+    idx_h = np.stack([g.choice(w.n_docs, size=k, replace=False) for _ in range(n_q)])
+    log(f"attend T=1 k={k} docs={w.n_docs} n_q={n_q}")
+    got, want = _attend_case(w, device, idx_h, 1, 9)
+    assert_attention_close(got, want)
+
+
 # a document id outside [0, n_docs) in one query's idx: that query's output is
 # NaN throughout (the kernel's own check; the host cannot read idx), the other
 # queries' outputs are as with valid ids
