@@ -730,6 +730,8 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
     int64_t c1[RPL];
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
+      c0[j] = c1[j] = 0;
+      if (64 * j >= a.k) break;  // (wave-uniform)
       const int r = lane + 64 * j;
       const bool bad_doc = r < a.k && (doc[j] < 0 || doc[j] >= a.n_docs);
       any_bad |= bad_doc;
@@ -740,6 +742,7 @@ __global__ __launch_bounds__(64 * DW) void attend_decode_kernel(AttendArgs a, in
     int carry = 0;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
+      if (64 * j >= a.k) break;
       const int r = lane + 64 * j;
       const int cnt = r < a.k ? (int)(c1[j] - c0[j]) : 0;
       int x = cnt;
