@@ -380,8 +380,10 @@ static_assert(RS_ITEMS == WS_ITEMS, "the resolve and the selection cover the sam
 
 // edge_range_score for N documents of one query with their loads batched (a
 // loop per document would wait on each one in turn): the chunk ranges, then
-// each document's stored score or first record, then one round per further
-// 32-chunk unit (loads clamped to the document's last unit, masked after)
+// in one round each document's stored score or first record together with
+// the records of its next EB units, then one round per further unit (loads
+// clamped to the document's last unit, masked after)
+constexpr int EB = 2;  // further units fetched with the first record (a document of <= 65 chunks)
 template <int N>
 __device__ __forceinline__ void edge_scores_batched(const EdgeLayout &L, const int64_t *doc_chunk_off, int n_docs,
                                                     int t_r, int q, const int (&doc)[N], float (&out)[N]) {
@@ -407,7 +409,17 @@ __device__ __forceinline__ void edge_scores_batched(const EdgeLayout &L, const i
     out[u] = *p;
     extra = max(extra, (int)(tb[u] - ta[u]));
   }
-  for (int e = 1; e <= extra; ++e) {
+  float xb[EB][N];
+#pragma unroll
+  for (int e = 1; e <= EB; ++e)
+#pragma unroll
+    for (int u = 0; u < N; ++u) xb[e - 1][u] = rec[min(ta[u] + e, tb[u]) * 32 + r];
+#pragma unroll
+  for (int e = 1; e <= EB; ++e)
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      if (ta[u] + e <= tb[u]) out[u] = fmaxf(out[u], xb[e - 1][u]);
+  for (int e = EB + 1; e <= extra; ++e) {
     float x[N];
 #pragma unroll
     for (int u = 0; u < N; ++u) x[u] = rec[min(ta[u] + e, tb[u]) * 32 + r];
