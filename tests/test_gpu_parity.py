@@ -437,14 +437,16 @@ def test_layer_sliced_topk_selected_in_attention(device, k):
     _check_sliced_layer(w, device)
 
 
-@pytest.mark.parametrize("n_q,t_r", [(20, 1), (3, 4)])
-def test_layer_sliced_multi_unit_documents(device, n_q, t_r):
+@pytest.mark.parametrize("n_q,t_r,long_chunks", [(20, 1, 40), (3, 4, 40), (20, 1, 130)])
+def test_layer_sliced_multi_unit_documents(device, n_q, t_r, long_chunks):
     # the same sliced layer with documents of 1-4 chunks and, every 500th, one
-    # of 40 chunks crossing 32-chunk units; 20 single-token queries (a second,
-    # partial block of 16) and 3 queries of 4 router tokens (a row block each)
-    g = np.random.default_rng(12 + n_q)
+    # of 40 chunks (two or three 32-chunk units: the resolve's first round of
+    # record loads) or 130 chunks (five or six units: its later rounds)
+    # crossing 32-chunk units; 20 single-token queries (a second, partial
+    # block of 16) and 3 queries of 4 router tokens (a row block each)
+    g = np.random.default_rng(12 + n_q + long_chunks)
     lens = g.integers(1, 65, size=8_400).astype(np.int64)
-    lens[::500] = 40 * 16 - 3
+    lens[::500] = long_chunks * 16 - 3
     w = _wl("decode-100m", 200_000, doc_lens=lens, chunk=16, h_kv=2, d=64, h_r=2, d_r=64, h_q=4, n_q=n_q, k=16,
             pos0=16, T_route=t_r, L_loc=t_r, gold=np.zeros((n_q, 0), dtype=np.int64))
     assert w.n_docs > 8192 and w.n_chunks > 2 * w.n_docs
