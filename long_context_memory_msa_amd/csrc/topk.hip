@@ -383,7 +383,7 @@ static_assert(RS_ITEMS == WS_ITEMS, "the resolve and the selection cover the sam
 // in one round each document's stored score or first record together with
 // the records of its next EB units, then one round per further unit (loads
 // clamped to the document's last unit, masked after)
-constexpr int EB = 2;  // further units fetched with the first record (a document of <= 65 chunks)
+constexpr int EB = 2;  // further units read with the first record: a document of <= 65 chunks needs no more
 template <int N>
 __device__ __forceinline__ void edge_scores_batched(const EdgeLayout &L, const int64_t *doc_chunk_off, int n_docs,
                                                     int t_r, int q, const int (&doc)[N], float (&out)[N]) {
