@@ -148,6 +148,58 @@ def _scan_block(bounds):
     return O.chunk_scores(_CPU_JOB["QR"], _CPU_JOB["krbar"][a:b])
 
 
+def _pool_block(bounds):
+    """Worker: the oracle's pooling of sample documents [a, b) (fp64, single thread)."""
+    import oracle as O
+
+    a, b = bounds
+    j = _CPU_JOB
+    t0, t1 = int(j["tok_off"][a]), int(j["tok_off"][b])
+    O.pool(j["lens"][a:b], j["chunk"], j["K"][t0:t1], j["V"][t0:t1], j["KR"][t0:t1], j["dtype"], j["base"])
+    return t1 - t0
+
+
+def cpu_pool_baseline(w, qi, n_docs: int, workers: int) -> dict:
+    """The fp64 oracle's offline pooling (oracle.pool) on the raw tokens of the
+    bank's first ``n_docs`` documents, one contiguous document range per forked
+    single-threaded worker; the rate is extrapolated to the whole bank (the
+    oracle's pooling time is linear in the tokens)."""
+    import multiprocessing
+
+    import numpy as np
+
+    from synth import rng, workloads as W
+
+    lens = w.doc_lens[:n_docs]
+    tok_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n_tok = int(tok_off[-1])
+    _CPU_JOB.update(lens=lens, tok_off=tok_off, chunk=w.chunk, dtype=w.dtype, base=w.rope_base,
+                    K=W.bank_raw(w, rng.ROLE_K, 0, n_tok), V=W.bank_raw(w, rng.ROLE_V, 0, n_tok),
+                    KR=W.bank_raw(w, rng.ROLE_KR, 0, n_tok, uhat=W.gold_uhat(w, qi["QR"])))
+    cuts = np.unique(np.linspace(0, n_docs, min(workers, n_docs) + 1).astype(np.int64))
+    blocks = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:])]
+    pool = multiprocessing.get_context("fork").Pool(len(blocks))
+    pool.map(int, range(len(blocks)))
+    t0 = time.perf_counter()
+    done = sum(pool.map(_pool_block, blocks, chunksize=1))
+    dt = time.perf_counter() - t0
+    pool.close()
+    pool.join()
+    _CPU_JOB.clear()
+    rate = done / dt
+    return {
+        "value": rate,
+        "unit": "tokens/s",
+        "cores": len(blocks),
+        "kind": "oracle",
+        "extrapolated_s_whole_bank": w.n_tok / rate,
+        "sample": (f"oracle pooling (fp64 NumPy: chunk means with document-wise RoPE, stored rounding, inverse "
+                   f"norms) of the raw K, V, K^R tokens of the first {n_docs} documents ({done} tokens) in "
+                   f"{len(blocks)} forked single-threaded processes, {dt:.2f} s wall; whole-bank time "
+                   f"extrapolated per token"),
+    }
+
+
 def cpu_baseline(w, qi, n_docs: int, workers: int) -> dict:
     """The fp64 oracle's layer forward on the first ``n_docs`` documents of the
     bank (pooled-shape synthetic values; the oracle's time does not depend on
@@ -594,7 +646,9 @@ def main() -> int:
         w = W.make_workload("decode-100m", bank_tokens=args.bank_tokens)
         workers = max(1, len(os.sched_getaffinity(0)))
         print(f"[bench] timing the oracle on {workers} host cores ...", file=sys.stderr, flush=True)
-        cpu_rec = cpu_baseline(w, W.query_inputs(w), args.cpu_docs, workers)
+        qi = W.query_inputs(w)
+        cpu_rec = cpu_baseline(w, qi, args.cpu_docs, workers)
+        cpu_rec["pool"] = cpu_pool_baseline(w, qi, 8 * workers, workers)
 
     import torch
 
@@ -740,7 +794,8 @@ def main() -> int:
                                        "GB/s": scan_bytes / (probe_ms * 1e-3) / 1e9,
                                        "frac_of_peak": scan_bytes / (probe_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                        "scan_frac_of_floor": probe_ms / route_ms}},
-        "pool": {"slabs": enc["slabs"], "GB/s": pool_gbs, "frac": pool_gbs / HBM_PEAK_GBS},
+        "pool": {"slabs": enc["slabs"], "GB/s": pool_gbs, "frac": pool_gbs / HBM_PEAK_GBS,
+                 "tokens_per_s": w.n_tok / pool_s},
         "gold_recovered": gold_ok,
     }
     if not (args.no_interleave and args.no_secondary):
